@@ -1,0 +1,146 @@
+"""CPU oracle for the paged KV write and paged varlen attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package; the product path (``paged_kv_attention_05_amd``) never
+does, and shares no code with it.
+
+The arithmetic lives in ``paged_oracle.c`` (plain float64 loops, written from the pages'
+``write_kv`` and ``ReferenceBackend.forward`` in "Engine v2: one core for every request",
+section "Attention over the pool"); this module only marshals numpy arrays into it.
+
+Arrays: float32 data is ``np.float32``; bfloat16 data is carried as its 16-bit patterns in
+``np.uint16`` and flagged with ``dtype="bf16"``.
+
+Every function here has a pin in ``tests/test_oracle_*.py`` that does not reuse this code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "paged_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_LIB = None
+
+DTYPES = {"f32": 0, "bf16": 1}
+
+
+def build(force: bool = False) -> str:
+    """Compile paged_oracle.c into liboracle.so with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """Load a compiled oracle library and declare its entry points."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.oracle_kv_write.restype = ctypes.c_int
+    lib.oracle_kv_write.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.oracle_gather_context.restype = None
+    lib.oracle_gather_context.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, P]
+    lib.oracle_paged_attention.restype = ctypes.c_int
+    lib.oracle_paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_double, P, P,
+                                           ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int32, P]
+    lib.oracle_round_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_to_bf16.argtypes = [ctypes.c_double]
+    return lib
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        build()
+        _LIB = load_library(_LIB_PATH)
+    return _LIB
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _check_data(a: np.ndarray, dtype: str, name: str) -> None:
+    want = np.float32 if dtype == "f32" else np.uint16
+    if a.dtype != want or not a.flags.c_contiguous:
+        raise TypeError(f"{name}: expected C-contiguous {np.dtype(want).name} for dtype {dtype}")
+
+
+def round_to_bf16(x: float) -> int:
+    """bfloat16 bit pattern of a float64 value, round-to-nearest-even."""
+    return int(_lib().oracle_round_to_bf16(float(x)))
+
+
+def kv_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache: np.ndarray,
+             v_cache: np.ndarray, in_dtype: str, cache_dtype: str) -> None:
+    """write_kv: copy k, v [N, Hkv, D] into the pools [NB+1, bs, Hkv, D] at the flat slots.
+
+    A negative slot goes to the pool's last slot.  Mutates k_cache and v_cache in place.
+    """
+    _check_data(k, in_dtype, "k")
+    _check_data(v, in_dtype, "v")
+    _check_data(k_cache, cache_dtype, "k_cache")
+    _check_data(v_cache, cache_dtype, "v_cache")
+    slot_mapping = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    n, hkv, d = k.shape
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    rc = _lib().oracle_kv_write(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                                n, hkv, d, num_slots, DTYPES[in_dtype], DTYPES[cache_dtype])
+    if rc != 0:
+        raise ValueError("oracle kv_write: slot out of range")
+
+
+def gather_context(cache: np.ndarray, table_row: np.ndarray, length: int, dtype: str) -> np.ndarray:
+    """First `length` rows of one request's context in logical order, float64 [length, Hkv, D]."""
+    _check_data(cache, dtype, "cache")
+    table_row = np.ascontiguousarray(table_row, dtype=np.int32)
+    bs, hkv, d = cache.shape[1], cache.shape[2], cache.shape[3]
+    out = np.empty((length, hkv, d), dtype=np.float64)
+    _lib().oracle_gather_context(_ptr(cache), _ptr(table_row), length, bs, hkv, d, DTYPES[dtype], _ptr(out))
+    return out
+
+
+def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                    query_start_loc: np.ndarray, seq_lens: np.ndarray, block_table: np.ndarray,
+                    scale: float, dtype: str, row_mask: Optional[np.ndarray] = None,
+                    want_f64: bool = False):
+    """ReferenceBackend.forward over the pool.
+
+    q [N, H, D]; caches [NB+1, bs, Hkv, D]; query_start_loc [R+1]; seq_lens [R];
+    block_table [R, W].  Returns out [N, H, D] in `dtype` (and the float64 result if
+    want_f64).  With row_mask, only the selected flattened rows are computed; the others
+    are left at zero (and NaN in the float64 result) so they cannot pass for results.
+    """
+    _check_data(q, dtype, "q")
+    _check_data(k_cache, dtype, "k_cache")
+    _check_data(v_cache, dtype, "v_cache")
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    n, h, d = q.shape
+    hkv, bs = k_cache.shape[2], k_cache.shape[1]
+    num_slots = k_cache.shape[0] * bs
+    out = np.zeros_like(q)
+    out64 = np.full(q.shape, np.nan, dtype=np.float64) if want_f64 else None
+    mask = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8)
+    rc = _lib().oracle_paged_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(qsl), _ptr(lens),
+                                       _ptr(table), bs, float(scale), _ptr(out), _ptr(out64),
+                                       len(lens), n, h, hkv, d, table.shape[1], num_slots,
+                                       DTYPES[dtype], _ptr(mask))
+    if rc == -1:
+        raise ValueError("oracle paged_attention: inconsistent batch metadata")
+    if rc != 0:
+        raise MemoryError("oracle paged_attention: allocation failed")
+    return (out, out64) if want_f64 else out

@@ -1,0 +1,221 @@
+/*
+ * CPU oracle for the paged KV write and for paged varlen attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call this file:
+ * only the test suite, the smoke check and the CPU-baseline leg of the benchmark use it.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Written from "Engine v2: one core for every request" (inference.shantanugoel.com,
+ * chapter 31), sections "Flattened ragged batches" (BatchMeta, the slot formula) and
+ * "Attention over the pool" (write_kv, ReferenceBackend.forward), with the gather step
+ * described in the vllm-lite README (section on the paged KV cache: slots are
+ * block_id * block_size + offset, read in logical order) and its grouped-query note
+ * (query heads fold contiguously onto KV heads, kv = h / (H / Hkv)).
+ *
+ * Everything is plain loops in float64, in the order the pages describe:
+ *   write:      for each new token i (increasing), slot = slot_mapping[i], a negative slot
+ *               is redirected to the pool's last slot, then the token's Hkv*D row is copied
+ *               (cast to the cache dtype) into that slot.
+ *   attention:  for each request r, gather its first seq_len context rows through its block
+ *               table (logical order), then for each of its t query rows i (position
+ *               seq_len - t + i) and each query head h: scores over keys 0..position, max,
+ *               exponentials, sum, weighted sum of V, divide.  Two passes, no tiling.
+ *               Requests with seq_len == 0 or no query rows leave their rows at zero.
+ *
+ * dtype codes: 0 = float32, 1 = bfloat16 (stored as the upper 16 bits of a float32).
+ * Rounding to an output dtype is round-to-nearest-even, done once from float64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Value of element idx of an array of the given dtype, exactly, as a double. */
+static double load_elem(const void* base, int64_t idx, int dtype) {
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 (ties to even), returned as its 16-bit pattern.
+ * Done directly from the double (no intermediate float rounding): the value is scaled so
+ * that one unit is the bfloat16 spacing at its binade (8 significant bits; spacing never
+ * below the subnormal step 2^-133), rounded with rint (ties-to-even in the default mode),
+ * and scaled back. */
+static uint16_t round_to_bf16(double x) {
+    if (isnan(x)) return (uint16_t)(signbit(x) ? 0xFFC0u : 0x7FC0u);
+    if (isinf(x)) return (uint16_t)(x > 0 ? 0x7F80u : 0xFF80u);
+    if (x == 0.0) return (uint16_t)(signbit(x) ? 0x8000u : 0x0000u);
+    int e;
+    (void)frexp(x, &e);                 /* x = m * 2^e, 0.5 <= |m| < 1 */
+    int q = e - 8;                      /* spacing of 8-significant-bit numbers in this binade */
+    if (q < -133) q = -133;
+    double r = ldexp(rint(ldexp(x, -q)), q);
+    const double max_bf16 = 3.38953138925153547590470800371487866880e38; /* (2 - 2^-7) * 2^127 */
+    float f;
+    if (fabs(r) > max_bf16) f = (r > 0) ? INFINITY : -INFINITY;
+    else f = (float)r;                  /* exact: r has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(bits >> 16);
+}
+
+static void store_elem(void* base, int64_t idx, int dtype, double x) {
+    if (dtype == ORACLE_F32) ((float*)base)[idx] = (float)x; /* C cast: round to nearest even */
+    else ((uint16_t*)base)[idx] = round_to_bf16(x);
+}
+
+/* bfloat16 pattern of a double, exposed so the rounding can be pinned on its own. */
+uint16_t oracle_round_to_bf16(double x) { return round_to_bf16(x); }
+
+/*
+ * write_kv ("Attention over the pool"): k, v are [N, Hkv, D] in in_dtype; the caches are
+ * [num_slots, Hkv, D] in cache_dtype (the pool [blocks, block_size, Hkv, D] seen as flat
+ * slots).  Returns 0, or -1 if a slot is out of range (nothing is written in that case).
+ */
+int oracle_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                    void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                    int64_t num_slots, int32_t in_dtype, int32_t cache_dtype) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    const int64_t scratch = num_slots - 1;
+    for (int64_t i = 0; i < num_tokens; ++i)
+        if (slot_mapping[i] >= num_slots) return -1;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        int64_t s = slot_mapping[i] >= 0 ? slot_mapping[i] : scratch;
+        for (int64_t e = 0; e < row; ++e) {
+            store_elem(k_cache, s * row + e, cache_dtype, load_elem(k, i * row + e, in_dtype));
+            store_elem(v_cache, s * row + e, cache_dtype, load_elem(v, i * row + e, in_dtype));
+        }
+    }
+    return 0;
+}
+
+/*
+ * gather_context: the first `length` token rows of a request, in logical order.  Position p
+ * lives at slot table[p / block_size] * block_size + p % block_size.  out is [length, Hkv, D].
+ */
+void oracle_gather_context(const void* cache, const int32_t* table_row, int32_t length,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t dtype, double* out) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    for (int32_t p = 0; p < length; ++p) {
+        int64_t slot = (int64_t)table_row[p / block_size] * block_size + p % block_size;
+        for (int64_t e = 0; e < row; ++e) out[(int64_t)p * row + e] = load_elem(cache, slot * row + e, dtype);
+    }
+}
+
+/*
+ * ReferenceBackend.forward ("Attention over the pool").
+ *
+ * q, out: [N, H, D] in dtype; caches: [num_slots, Hkv, D] in dtype; query_start_loc [R+1];
+ * seq_lens [R]; block_table [R, stride].  scale multiplies every score.
+ * out_f64, if not NULL, receives the unrounded float64 result ([N, H, D]).
+ * row_mask, if not NULL, selects the flattened rows to compute ([N] bytes, nonzero = compute);
+ * rows not selected are left untouched in both outputs.
+ * Returns 0, or -1 on inconsistent metadata (then nothing is written).
+ */
+int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t block_size, double scale, void* out,
+                           double* out_f64, int32_t num_reqs, int64_t num_tokens,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_table_stride, int64_t num_slots, int32_t dtype,
+                           const uint8_t* row_mask) {
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0) return -1;
+    if (query_start_loc[0] != 0 || query_start_loc[num_reqs] != num_tokens) return -1;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        int32_t t = query_start_loc[r + 1] - query_start_loc[r];
+        int32_t len = seq_lens[r];
+        if (t < 0 || len < 0) return -1;
+        if (len > 0 && t > len) return -1;
+        int32_t nblk = (len + block_size - 1) / block_size;
+        if (nblk > block_table_stride) return -1;
+        for (int32_t b = 0; b < nblk; ++b) {
+            int64_t blk = block_table[(int64_t)r * block_table_stride + b];
+            if (blk < 0 || (blk + 1) * block_size > num_slots) return -1;
+        }
+    }
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t qrow = (int64_t)num_heads * head_dim;
+    const int64_t kvrow = (int64_t)num_kv_heads * head_dim;
+
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        const int32_t begin = query_start_loc[r], end = query_start_loc[r + 1];
+        const int32_t length = seq_lens[r];
+        if (length == 0 || begin == end) {          /* padding row: output stays zero */
+            for (int64_t i = begin; i < end; ++i) {
+                if (row_mask && !row_mask[i]) continue;
+                for (int64_t e = 0; e < qrow; ++e) {
+                    store_elem(out, i * qrow + e, dtype, 0.0);
+                    if (out_f64) out_f64[i * qrow + e] = 0.0;
+                }
+            }
+            continue;
+        }
+        const int32_t t = end - begin;
+        int any = 0;
+        for (int32_t i = 0; i < t && !any; ++i) any = !row_mask || row_mask[begin + i];
+        if (!any) continue;
+
+        const int32_t* table_row = block_table + (int64_t)r * block_table_stride;
+        double* ctx_k = (double*)malloc(sizeof(double) * (size_t)length * (size_t)kvrow);
+        double* ctx_v = (double*)malloc(sizeof(double) * (size_t)length * (size_t)kvrow);
+        if (!ctx_k || !ctx_v) { free(ctx_k); free(ctx_v); return -2; }
+        oracle_gather_context(k_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_k);
+        oracle_gather_context(v_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_v);
+
+        int failed = 0;
+        #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+        for (int32_t i = 0; i < t; ++i) {
+            for (int32_t h = 0; h < num_heads; ++h) {
+                const int64_t row = (int64_t)begin + i;
+                if (row_mask && !row_mask[row]) continue;
+                const int32_t kvh = h / group;
+                const int32_t q_pos = length - t + i;       /* the last t positions of the context */
+                double* s = (double*)malloc(sizeof(double) * (size_t)(q_pos + 1));
+                double* acc = (double*)calloc((size_t)head_dim, sizeof(double));
+                double* qv = (double*)malloc(sizeof(double) * (size_t)head_dim);
+                if (!s || !acc || !qv) {
+                    free(s); free(acc); free(qv);
+                    #pragma omp atomic write
+                    failed = 1;
+                    continue;
+                }
+                for (int32_t d = 0; d < head_dim; ++d) qv[d] = load_elem(q, row * qrow + (int64_t)h * head_dim + d, dtype);
+                /* pass 1: scores of keys 0 .. q_pos and their maximum */
+                double m = -INFINITY;
+                for (int32_t j = 0; j <= q_pos; ++j) {
+                    const double* kj = ctx_k + (int64_t)j * kvrow + (int64_t)kvh * head_dim;
+                    double dot = 0.0;
+                    for (int32_t d = 0; d < head_dim; ++d) dot += qv[d] * kj[d];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                /* pass 2: exponentials, their sum and the weighted sum of V */
+                double l = 0.0;
+                for (int32_t j = 0; j <= q_pos; ++j) {
+                    const double w = exp(s[j] - m);
+                    const double* vj = ctx_v + (int64_t)j * kvrow + (int64_t)kvh * head_dim;
+                    l += w;
+                    for (int32_t d = 0; d < head_dim; ++d) acc[d] += w * vj[d];
+                }
+                for (int32_t d = 0; d < head_dim; ++d) {
+                    const double o = acc[d] / l;
+                    const int64_t idx = row * qrow + (int64_t)h * head_dim + d;
+                    store_elem(out, idx, dtype, o);
+                    if (out_f64) out_f64[idx] = o;
+                }
+                free(s); free(acc); free(qv);
+            }
+        }
+        free(ctx_k);
+        free(ctx_v);
+        if (failed) return -2;
+    }
+    return 0;
+}
