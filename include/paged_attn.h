@@ -1,0 +1,140 @@
+/*
+ * paged_attn.h: C ABI of the paged KV write and paged varlen attention library
+ * (libpagedattn.so, HIP for gfx950).
+ *
+ * The operations are the attention backend of "Engine v2: one core for every request"
+ * (inference.shantanugoel.com, chapter 31): write_kv and ReferenceBackend.forward in section
+ * "Attention over the pool", with the batch described by BatchMeta in section "Flattened
+ * ragged batches".
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, on the current HIP device; pointers are device
+ *     pointers unless the name ends in _host.  The caller allocates and owns every buffer,
+ *     including the workspace; the library never allocates device memory, never frees, and
+ *     keeps no pointer after returning.
+ *   - dtype codes: PA_DTYPE_F32 (IEEE float32) and PA_DTYPE_BF16 (bfloat16).
+ *   - Work is enqueued on `stream` and is asynchronous; nothing synchronises the device.
+ *     The KV write of a step must be enqueued before the attention that reads it, on the
+ *     same stream (a row's own key is in its visible range, and a block adopted from the
+ *     prefix cache may be written in the same step).
+ *   - Return value: PA_OK (0) on success, a negative PA_ERR_* code otherwise; then nothing
+ *     was enqueued (except for PA_ERR_LAUNCH) and paged_attn_last_error() describes why.
+ *     Validation reads only the host copies of the metadata.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* unsupported or inconsistent sizes (heads, head_dim, block_size) */
+#define PA_ERR_DTYPE (-3)       /* unknown dtype code, or a combination not supported */
+#define PA_ERR_METADATA (-4)    /* query_start_loc / seq_lens / table width inconsistent */
+#define PA_ERR_WORKSPACE (-5)   /* workspace smaller than paged_attention_workspace_bytes() */
+#define PA_ERR_LAUNCH (-6)      /* a kernel launch failed (hipGetLastError reported it) */
+#define PA_ERR_RANGE (-7)       /* debug checks only: slot or block id out of range, duplicate slot */
+
+#define PA_DTYPE_F32 0
+#define PA_DTYPE_BF16 1
+
+/*
+ * paged_kv_write: write_kv of "Attention over the pool".
+ *
+ * For every new token i < num_tokens, its K row k[i] and V row v[i] (each num_kv_heads *
+ * head_dim elements, layout [num_tokens, num_kv_heads, head_dim], dtype in_dtype) are
+ * copied into row s of the pools k_cache / v_cache seen as [num_slots, num_kv_heads,
+ * head_dim] (the pool [num_blocks + 1, block_size, num_kv_heads, head_dim], num_slots =
+ * (num_blocks + 1) * block_size), where s = slot_mapping[i] (int64) if it is >= 0 and
+ * s = num_slots - 1 (the scratch slot of the pool's extra last block) if it is negative:
+ * padding rows carry slot -1.  Values are cast to cache_dtype with round-to-nearest-even
+ * when the dtypes differ; otherwise the copy is bit-exact.  Every other pool element is
+ * left unchanged.
+ *
+ * Preconditions (not checked unless debug checks are on): slot_mapping[i] < num_slots, and
+ * non-negative slots are distinct (several padding rows may share the scratch slot, whose
+ * content is then one of theirs).
+ */
+int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_slots, int32_t in_dtype, int32_t cache_dtype, hipStream_t stream);
+
+/*
+ * paged_attention_workspace_bytes: device workspace paged_attention_varlen needs for this
+ * batch (same arguments as there).  Depends only on the host metadata; returns 0 when the
+ * arguments are invalid (the attention call would then report why).
+ */
+size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       const int32_t* query_start_loc_host,
+                                       const int32_t* seq_lens_host, int32_t dtype);
+
+/*
+ * paged_attention_varlen: ReferenceBackend.forward of "Attention over the pool", over one
+ * flattened ragged batch (BatchMeta of "Flattened ragged batches").
+ *
+ *   q, out            [num_tokens, num_heads, head_dim], dtype.  out is fully written.
+ *   k_cache, v_cache  [num_slots / block_size, block_size, num_kv_heads, head_dim], dtype;
+ *                     read only.
+ *   query_start_loc   [num_reqs + 1] int32: request r owns flattened rows
+ *                     query_start_loc[r] .. query_start_loc[r+1]-1 (t_r rows).
+ *   seq_lens          [num_reqs] int32: context length L_r including this step's tokens.
+ *   block_table       [num_reqs, block_table_stride] int32: physical block ids of request r
+ *                     in logical order; entries past ceil(L_r / block_size) are never read.
+ *   *_host            host copies of query_start_loc and seq_lens (must equal the device
+ *                     arrays); max_query_len / max_seq_len are their maxima (informational).
+ *
+ * Row i of request r is at position L_r - t_r + i and attends keys 0 .. that position:
+ *     out[row, h, :] = sum_j softmax_j(scale * <q[row, h, :], K_j>) V_j,
+ * where K_j / V_j is position j of the request read from slot
+ * block_table[r][j / block_size] * block_size + j % block_size, head kv = h / (H / Hkv)
+ * (query heads grouped contiguously onto KV heads).  Requests with seq_len 0 or no rows
+ * (padding) produce zero rows.  Arithmetic is float32 (bfloat16 inputs feed bf16 matrix
+ * cores with float32 accumulation; probabilities are rounded to bf16 for the PV product);
+ * out is rounded to nearest-even.
+ *
+ * Supported: head_dim a multiple of 8, 8..256; block_size >= 1 (the bf16 matrix-core
+ * paths need block_size 16 and head_dim 64 or 128; other shapes use the vector path);
+ * num_heads % num_kv_heads == 0.  workspace must hold paged_attention_workspace_bytes().
+ *
+ * Preconditions not checked (unless debug checks are on): block ids in range; the K/V
+ * of every visible position has been written.
+ */
+int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t block_size, float scale, void* out,
+                           int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                           int64_t num_slots, const int32_t* query_start_loc_host,
+                           const int32_t* seq_lens_host, int32_t max_query_len,
+                           int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, hipStream_t stream);
+
+/*
+ * paged_attn_set_debug_checks: when enable != 0, later calls on this thread also copy
+ * slot_mapping / block_table to the host (synchronously) and check the preconditions
+ * above, returning PA_ERR_RANGE on a violation.  Off by default.
+ */
+void paged_attn_set_debug_checks(int32_t enable);
+
+/* Description of the last non-zero return on this thread ("" if none). */
+const char* paged_attn_last_error(void);
+
+/*
+ * Selects the attention kernels (for tests and measurement): 0 = automatic (default),
+ * 1 = vector-ALU tile kernel for every request.  Applies to later calls on this thread.
+ */
+void paged_attn_set_path(int32_t path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,160 @@
+"""Paged KV write and paged varlen attention for MI355X (gfx950), behind a C ABI.
+
+This module only marshals torch tensors into ``libpagedattn.so`` (built in place by
+``build.py``); every step of the computation runs in its HIP kernels.  Torch supplies
+device memory and the current stream.  If the library is missing, every call raises:
+there is no fallback.
+
+Names follow the C ABI in ``include/paged_attn.h``:
+    paged_kv_write(k, v, slot_mapping, k_cache, v_cache)
+    paged_attention_varlen(q, k_cache, v_cache, query_start_loc, seq_lens, block_table,
+                           block_size, scale, out, query_start_loc_host=..., seq_lens_host=...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
+          -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
+EXPORTS = ["paged_kv_write", "paged_attention_varlen", "paged_attention_workspace_bytes",
+           "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path"]
+
+_lib = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedattn.so and declare its entry points (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, P]
+    lib.paged_attention_workspace_bytes.restype = SZ
+    lib.paged_attention_workspace_bytes.argtypes = [I32, I64, I32, I32, I32, I32, P, P, I32]
+    lib.paged_attention_varlen.restype = ctypes.c_int
+    lib.paged_attention_varlen.argtypes = [P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I64, I32, I32,
+                                           I32, I32, I64, P, P, I32, I32, P, SZ, I32, P]
+    lib.paged_attn_last_error.restype = ctypes.c_char_p
+    lib.paged_attn_last_error.argtypes = []
+    lib.paged_attn_set_debug_checks.restype = None
+    lib.paged_attn_set_debug_checks.argtypes = [I32]
+    lib.paged_attn_set_path.restype = None
+    lib.paged_attn_set_path.argtypes = [I32]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise PagedAttnError(rc, load_library().paged_attn_last_error().decode())
+
+
+def _dptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _host_i32(x: Sequence[int]):
+    arr = (ctypes.c_int32 * len(x))(*[int(v) for v in x])
+    return arr
+
+
+def set_debug_checks(enable: bool) -> None:
+    load_library().paged_attn_set_debug_checks(1 if enable else 0)
+
+
+def set_path(path: int) -> None:
+    """0: automatic kernel choice; 1: vector-ALU tile kernel for every request."""
+    load_library().paged_attn_set_path(int(path))
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, stream=None) -> None:
+    """Scatter k, v [N, Hkv, D] into the pools [NB+1, bs, Hkv, D] at slot_mapping (int64)."""
+    lib = load_library()
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    n, hkv, d = k.shape
+    if v.shape != k.shape or k_cache.shape != v_cache.shape or tuple(k_cache.shape[2:]) != (hkv, d):
+        raise ValueError("shape mismatch between k, v and the caches")
+    if k.dtype != v.dtype or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k and v (and the two caches) must share a dtype")
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    _check(lib.paged_kv_write(_dptr(k, "k"), _dptr(v, "v"), _dptr(slot_mapping, "slot_mapping"),
+                              _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"), n, hkv, d, num_slots,
+                              PA_DTYPE[k.dtype], PA_DTYPE[k_cache.dtype], _stream(stream)))
+
+
+def paged_attention_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                                    query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
+                                    dtype: torch.dtype) -> int:
+    lib = load_library()
+    r = len(seq_lens_host)
+    n = int(query_start_loc_host[-1]) if r else 0
+    return int(lib.paged_attention_workspace_bytes(r, n, num_heads, num_kv_heads, head_dim, block_size,
+                                                   _host_i32(query_start_loc_host), _host_i32(seq_lens_host),
+                                                   PA_DTYPE[dtype]))
+
+
+def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           query_start_loc: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor,
+                           block_size: int, scale: float, out: Optional[torch.Tensor] = None, *,
+                           query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
+                           max_query_len: int = 0, max_seq_len: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of the flattened batch over the pool; returns out [N, H, D]."""
+    lib = load_library()
+    n, h, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[1] != block_size or k_cache.shape[3] != d:
+        raise ValueError("cache shape must be [num_blocks + 1, block_size, Hkv, D]")
+    if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
+        raise ValueError("q and the caches must share a dtype")
+    for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens), ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    hkv = k_cache.shape[2]
+    r = len(seq_lens_host)
+    qh, sh = _host_i32(query_start_loc_host), _host_i32(seq_lens_host)
+    need = lib.paged_attention_workspace_bytes(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype])
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    stride = block_table.shape[1] if block_table.dim() == 2 else 0
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    _check(lib.paged_attention_varlen(
+        _dptr(q, "q"), _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"),
+        _dptr(query_start_loc, "query_start_loc"), _dptr(seq_lens, "seq_lens"), _dptr(block_table, "block_table"),
+        block_size, float(scale), _dptr(out, "out"), r, n, h, hkv, d, stride, num_slots, qh, sh,
+        int(max_query_len), int(max_seq_len), _dptr(workspace, "workspace"), workspace.numel(),
+        PA_DTYPE[q.dtype], _stream(stream)))
+    return out

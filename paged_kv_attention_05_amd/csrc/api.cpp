@@ -1,0 +1,222 @@
+// C ABI of libpagedattn.so: argument validation (host copies only), the work plan, and the
+// launches.  The operations and their arguments are those of write_kv / ReferenceBackend in
+// "Engine v2: one core for every request" (sections "Flattened ragged batches" and
+// "Attention over the pool"); see include/paged_attn.h for the contract.
+#include "paged_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+bool valu_head_dim_supported(int32_t D);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local int g_debug_checks = 0;
+thread_local int g_path = 0;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the host metadata and builds the plan.  Returns PA_OK or an error code.
+int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t bs, int32_t stride,
+              const int32_t* qsl, const int32_t* lens, int32_t dtype, pa::Plan* out) {
+  if (R < 0 || N < 0) return fail(PA_ERR_METADATA, "num_reqs and num_tokens must be >= 0");
+  if (N > INT32_MAX) return fail(PA_ERR_SHAPE, "num_tokens must fit in int32");
+  if (H <= 0 || Hkv <= 0 || H % Hkv != 0)
+    return fail(PA_ERR_SHAPE, "num_heads must be a positive multiple of num_kv_heads");
+  if (!pa::valu_head_dim_supported(D))
+    return fail(PA_ERR_SHAPE, "head_dim must be one of 8, 16, 32, 48, 64, 96, 128, 256");
+  if (bs <= 0) return fail(PA_ERR_SHAPE, "block_size must be >= 1");
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "unknown dtype code");
+  if (R > 0 && (!qsl || !lens)) return fail(PA_ERR_NULL, "host copies of query_start_loc / seq_lens are required");
+  if (R == 0) {
+    if (N != 0) return fail(PA_ERR_METADATA, "num_tokens > 0 with no requests");
+  } else {
+    if (qsl[0] != 0) return fail(PA_ERR_METADATA, "query_start_loc[0] must be 0");
+    if ((int64_t)qsl[R] != N) return fail(PA_ERR_METADATA, "query_start_loc[num_reqs] must equal num_tokens");
+  }
+  pa::Plan p{};
+  p.R = R; p.H = H; p.Hkv = Hkv; p.g = H / Hkv; p.D = D; p.bs = bs;
+  if (p.g >= pa::kCols) { p.tile_heads = pa::kCols; p.tile_tokens = 1; }
+  else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
+  p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
+  const bool auto_path = g_path == 0;
+  p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
+                    ? pa::prefill_tile_tokens(p.g) : 0;
+  p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs)) ? 1 : 0;
+
+  // pass 1: validate and measure the small-tile work to size the key splits
+  double small_keys = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t t = qsl[r + 1] - qsl[r];
+    const int32_t L = lens[r];
+    if (t < 0) return fail(PA_ERR_METADATA, "query_start_loc must be non-decreasing (request " + std::to_string(r) + ")");
+    if (L < 0) return fail(PA_ERR_METADATA, "seq_lens must be >= 0 (request " + std::to_string(r) + ")");
+    if (L > 0 && t > L)
+      return fail(PA_ERR_METADATA, "request " + std::to_string(r) + " has more query rows than its seq_len");
+    if ((int64_t)(L + bs - 1) / bs > stride)
+      return fail(PA_ERR_METADATA, "block_table_stride too small for seq_len of request " + std::to_string(r));
+    if (t > 0 && L > 0 && !pa::use_prefill_path(p, t, L))
+      small_keys += (double)L * ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+  }
+  // Key splits: enough workgroups to fill 256 compute units several times over, but at
+  // most 1024 keys per split so long contexts are cut into balanced pieces.
+  const double target = small_keys * Hkv / 2048.0;
+  int32_t split = 64;
+  while (split < 1024 && (double)split * 2 <= target) split *= 2;
+  p.split_keys = split;
+
+  int64_t ns = 0, nm = 0, np = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    int32_t a, b, c, d;
+    pa::request_counts(p, qsl[r + 1] - qsl[r], lens[r], &a, &b, &c, &d);
+    ns += a; nm += b; np += c;
+  }
+  if (ns > INT32_MAX / 2 || nm > INT32_MAX / 2 || np > INT32_MAX / 2)
+    return fail(PA_ERR_SHAPE, "batch too large for the work lists");
+  p.n_small = ns; p.n_merge = nm; p.n_pf = np;
+
+  size_t off = 0;
+  p.off_req = off;   off = align_up(off + sizeof(pa::ReqOffsets) * (size_t)(R + 1), 256);
+  p.off_small = off; off = align_up(off + sizeof(pa::SmallItem) * (size_t)ns, 256);
+  p.off_merge = off; off = align_up(off + sizeof(pa::MergeItem) * (size_t)nm, 256);
+  p.off_pf = off;    off = align_up(off + sizeof(pa::PfItem) * (size_t)np, 256);
+  const size_t nparts = nm > 0 ? (size_t)ns * Hkv * pa::kCols : 0;
+  p.off_pm = off;    off = align_up(off + 4 * nparts, 256);
+  p.off_pl = off;    off = align_up(off + 4 * nparts, 256);
+  p.off_pacc = off;  off = align_up(off + 4 * nparts * (size_t)D, 256);
+  p.total_bytes = off;
+  *out = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_attn_last_error(void) { return g_last_error.c_str(); }
+
+void paged_attn_set_debug_checks(int32_t enable) { g_debug_checks = enable != 0; }
+
+void paged_attn_set_path(int32_t path) { g_path = path; }
+
+int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                   int64_t num_slots, int32_t in_dtype, int32_t cache_dtype, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads and head_dim must be > 0");
+  if (num_slots < 1) return fail(PA_ERR_SHAPE, "num_slots must be >= 1 (the scratch slot)");
+  if ((in_dtype != PA_DTYPE_F32 && in_dtype != PA_DTYPE_BF16) ||
+      (cache_dtype != PA_DTYPE_F32 && cache_dtype != PA_DTYPE_BF16))
+    return fail(PA_ERR_DTYPE, "unknown dtype code");
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_NULL, "null pointer argument");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row > INT32_MAX) return fail(PA_ERR_SHAPE, "num_kv_heads * head_dim too large");
+  if (g_debug_checks) {
+    std::vector<int64_t> s((size_t)num_tokens);
+    if (hipMemcpy(s.data(), slot_mapping, sizeof(int64_t) * s.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "debug check: copy of slot_mapping failed");
+    std::unordered_set<int64_t> seen;
+    for (size_t i = 0; i < s.size(); ++i) {
+      if (s[i] >= num_slots) return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] out of range");
+      if (s[i] >= 0 && !seen.insert(s[i]).second)
+        return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] repeats a slot");
+    }
+  }
+  const hipError_t e = pa::launch_kv_write(k, v, slot_mapping, k_cache, v_cache, num_tokens, (int32_t)row,
+                                           num_slots, in_dtype, cache_dtype, stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("kv write launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                       int32_t dtype) {
+  pa::Plan p;
+  const std::string keep = g_last_error;
+  const int rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, INT32_MAX,
+                           query_start_loc_host, seq_lens_host, dtype, &p);
+  g_last_error = keep;
+  return rc == PA_OK ? p.total_bytes : 0;
+}
+
+int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t block_size, float scale, void* out,
+                           int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                           int64_t num_slots, const int32_t* query_start_loc_host,
+                           const int32_t* seq_lens_host, int32_t max_query_len,
+                           int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, hipStream_t stream) {
+  g_last_error.clear();
+  (void)max_query_len;
+  (void)max_seq_len;
+  if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
+  pa::Plan p;
+  int rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                     query_start_loc_host, seq_lens_host, dtype, &p);
+  if (rc != PA_OK) return rc;
+  if (num_reqs == 0) return PA_OK;
+  if (!query_start_loc || !seq_lens || !block_table || !workspace) return fail(PA_ERR_NULL, "null pointer argument");
+  if (num_tokens > 0 && (!q || !out || !k_cache || !v_cache)) return fail(PA_ERR_NULL, "null pointer argument");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "q, out, caches and workspace must be 16-byte aligned");
+  if (num_slots < block_size || num_slots % block_size != 0)
+    return fail(PA_ERR_SHAPE, "num_slots must be a positive multiple of block_size");
+  if (workspace_bytes < p.total_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.total_bytes) + " bytes");
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
+  if (g_debug_checks) {
+    std::vector<int32_t> tb((size_t)num_reqs * block_table_stride);
+    if (!tb.empty() && hipMemcpy(tb.data(), block_table, sizeof(int32_t) * tb.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "debug check: copy of block_table failed");
+    const int64_t nb = num_slots / block_size;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      const int32_t used = (seq_lens_host[r] + block_size - 1) / block_size;
+      for (int32_t j = 0; j < used; ++j) {
+        const int32_t blk = tb[(size_t)r * block_table_stride + j];
+        if (blk < 0 || blk >= nb)
+          return fail(PA_ERR_RANGE, "block_table[" + std::to_string(r) + "][" + std::to_string(j) + "] out of range");
+      }
+    }
+  }
+  pa::AttnArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.qsl = query_start_loc; a.seq_lens = seq_lens; a.block_table = block_table; a.out = out;
+  a.bs = block_size; a.stride = block_table_stride; a.H = num_heads; a.Hkv = num_kv_heads;
+  a.g = p.g; a.D = head_dim; a.tile_tokens = p.tile_tokens; a.tile_heads = p.tile_heads;
+  a.split_keys = p.split_keys;
+  a.scale_log2e = scale * 1.4426950408889634f;
+
+  hipError_t e = pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream);
+  if (e == hipSuccess && p.n_pf > 0) e = pa::launch_prefill_mfma(p, a, workspace, stream);
+  if (e == hipSuccess && p.n_small > 0)
+    e = p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)
+                           : pa::launch_small_valu(p, a, workspace, dtype, stream);
+  if (e == hipSuccess && p.n_merge > 0) e = pa::launch_merge(p, a, workspace, dtype, stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("attention launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

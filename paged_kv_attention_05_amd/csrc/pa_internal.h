@@ -1,0 +1,124 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kCols = 16;          // query columns (token, head) of one small tile
+
+// ---------------------------------------------------------------- element conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bfloat16 bits, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+};
+
+// ---------------------------------------------------------------- work decomposition
+// A "small tile" is up to 16 query columns of one request and one KV head: `tile_tokens`
+// consecutive query rows times `tile_heads` of the KV head's query heads, over one key
+// split.  A "prefill tile" is `pf_tokens` consecutive rows times all query heads of one KV
+// head (a bf16 matrix-core tile); it covers all keys in one pass.
+struct Plan {
+  int32_t R, H, Hkv, g, D, bs;
+  int32_t tile_tokens, tile_heads, hsubs;
+  int32_t split_keys;              // keys per split of a small tile
+  int32_t pf_tokens;               // 0: prefill path off
+  int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
+  int64_t n_small, n_merge, n_pf;  // item counts (host-computed)
+  // workspace layout (byte offsets)
+  size_t off_req, off_small, off_merge, off_pf, off_pm, off_pl, off_pacc, total_bytes;
+};
+
+struct alignas(16) SmallItem {
+  int32_t r, tok0, hsub, split;
+  int32_t nsplit, first, pad0, pad1;   // first: index of the tile's split 0 (partials base)
+};
+struct alignas(16) MergeItem {
+  int32_t r, tok0, hsub, first;
+  int32_t nsplit, pad0, pad1, pad2;
+};
+struct alignas(8) PfItem {
+  int32_t r, tok0;
+};
+// per-request offsets written by the planner (exclusive scans)
+struct alignas(16) ReqOffsets {
+  int32_t small, merge, pf, nsplit;
+};
+
+// Classification of request r, identical on host and device.
+__host__ __device__ __forceinline__ bool use_prefill_path(const Plan& p, int32_t t, int32_t L) {
+  return p.pf_tokens > 0 && L > 0 && t * p.g > kCols;
+}
+__host__ __device__ __forceinline__ int32_t small_nsplit(const Plan& p, int32_t L) {
+  return L <= 0 ? 1 : (L + p.split_keys - 1) / p.split_keys;
+}
+__host__ __device__ __forceinline__ void request_counts(const Plan& p, int32_t t, int32_t L,
+                                                        int32_t* n_small, int32_t* n_merge,
+                                                        int32_t* n_pf, int32_t* nsplit) {
+  *n_small = *n_merge = *n_pf = 0;
+  *nsplit = 1;
+  if (t <= 0) return;
+  if (use_prefill_path(p, t, L)) {
+    *n_pf = (t + p.pf_tokens - 1) / p.pf_tokens;
+    return;
+  }
+  const int32_t tiles = ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+  const int32_t ns = small_nsplit(p, L);
+  *nsplit = ns;
+  *n_small = tiles * ns;
+  *n_merge = ns > 1 ? tiles : 0;
+}
+
+// Arguments common to the attention kernels.
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  void* out;
+  int32_t bs, stride, H, Hkv, g, D;
+  int32_t tile_tokens, tile_heads, split_keys;
+  float scale_log2e;                 // scale * log2(e): scores are kept in base 2
+};
+
+struct Partials {
+  float* m;      // [n_small * Hkv * 16]
+  float* l;      // [n_small * Hkv * 16]
+  float* acc;    // [n_small * Hkv * 16 * D]
+};
+
+// ---------------------------------------------------------------- launchers (host)
+hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, void* kc, void* vc,
+                           int64_t n, int32_t row_elems, int64_t num_slots, int32_t in_dtype,
+                           int32_t cache_dtype, hipStream_t s);
+hipError_t launch_plan(const Plan& p, const int32_t* qsl, const int32_t* seq_lens, void* ws, hipStream_t s);
+hipError_t launch_small_valu(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
+hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
+hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
+hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
+bool small_mfma_supported(int32_t D, int32_t bs);
+bool prefill_mfma_supported(int32_t D, int32_t bs, int32_t g);
+int32_t prefill_tile_tokens(int32_t g);
+
+}  // namespace pa

@@ -65,3 +65,32 @@ def sdpa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, co
     y = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
                                                          enable_gqa=True)
     return y[0].permute(1, 0, 2).numpy()
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def attention_error(got: np.ndarray, ref64: np.ndarray, dtype: str) -> float:
+    """Error of a GPU attention output against the float64 oracle, as a multiple of the bound.
+
+    float32: |got - ref| <= 1e-5 * max|ref| over the (row, head) vector, since outputs are
+    convex combinations of V rows and may cross zero.
+    bfloat16: |got - ref| <= 2e-2 + half a bfloat16 ulp of ref (the rounding of the stored
+    output alone can exceed 2e-2 once |ref| >= 8).
+    Returns max(error / bound); <= 1 passes.  NaN anywhere returns inf.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)) or not np.all(np.isfinite(ref64)):
+        return float("inf")
+    diff = np.abs(got - ref64)
+    if dtype == "f32":
+        bound = 1e-5 * np.maximum(np.abs(ref64).max(axis=-1, keepdims=True), 1e-30)
+    else:
+        bound = 2e-2 + 0.5 * bf16_ulp(ref64)
+    return float((diff / bound).max())
