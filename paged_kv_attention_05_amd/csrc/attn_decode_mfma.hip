@@ -1,5 +1,268 @@
+// Small-tile paged attention on bf16 matrix cores: the decode path (and any request whose
+// rows times grouped heads fit 16 query columns: decodes, speculative-verification rows).
+//
+// Same contract and work items as the vector kernel (attn_valu.hip): one workgroup of four
+// waves takes up to 16 query columns (token, head) of one request and one KV head over one
+// split of the keys; the split-K partials are combined by the shared merge kernel.  Decode
+// reads the whole history once per step, so this kernel is built to stream K/V: every
+// key's row of one KV head is read exactly once per tile, with the query heads of the
+// group as the 16 columns (grouped-query attention folds heads instead of repeating K, as
+// in the vllm-lite README's note), and the blocks of a table are read in place (slot-major
+// pool: a 16-token block of one KV head is 16 rows of D contiguous elements).
+//
+// Per wave and 16-key block (one pool block at block_size 16):
+//   S^T[key][col] = K[key][:] . Q[col][:]   mfma_f32_16x16x32_bf16, K straight from HBM into
+//                                           the A operand (lane: key = lane%16, 8 dims),
+//                                           Q^T held in registers as the B operand.
+//   online softmax per column               the lane owning column n keeps its running max;
+//                                           the 4 lane groups share it with two xor shuffles.
+//   O^T[d][col] += V^T[d][key] P^T[key][col] mfma_f32_16x16x16 bf16: P^T is the S^T
+//                                           accumulator layout itself; V^T is read from a
+//                                           padded LDS copy of the block with the gfx950
+//                                           LDS transpose read (ds_read_tr16_b64).
+// P is split into bf16 high and low parts (two products) so the probabilities keep ~16
+// bits: cheap here, since the path is bound by HBM, not by the matrix cores.
+// The next block's K and V are loaded into registers while the current one is computed.
 #include "pa_internal.h"
+
 namespace pa {
-bool small_mfma_supported(int32_t, int32_t) { return false; }
-hipError_t launch_small_mfma(const Plan&, const AttnArgs&, void*, hipStream_t) { return hipErrorInvalidValue; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kBlk = 16;                      // keys per block (block_size)
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int KC = D / 32;           // k-chunks of the QK^T product
+  static constexpr int DT = D / 16;           // 16-wide d tiles of the PV product
+  static constexpr int PITCH = D + 16;        // LDS row pitch (elements): conflict-free transpose reads
+  static constexpr int VPIECES = D / 8;       // 16-byte pieces per V row
+  static constexpr int VLOADS = kBlk * VPIECES / 64;   // 16-byte loads per lane per V block
+  static constexpr int VBUF = kBlk * PITCH;   // elements of one wave's V buffer
+};
+
+__device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
+                                                       Partials part) {
+  using C = DecodeCfg<D>;
+  // V staging (per wave) and, after the key loop, the per-wave output slabs.
+  constexpr int kVBytes = 4 * C::VBUF * 2;
+  constexpr int kSlabBytes = 4 * kCols * D * 4;
+  __shared__ __align__(16) unsigned char smem[kVBytes > kSlabBytes ? kVBytes : kSlabBytes];
+  __shared__ float sM[4][kCols], sL[4][kCols], sTot[kCols], sMax[kCols];
+
+  const SmallItem it = items[blockIdx.x];
+  const int hkv = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b, L = a.seq_lens[it.r], c = L - t;
+  const int32_t Tn = min(a.tile_tokens, t - it.tok0);
+  const int32_t h0 = it.hsub * a.tile_heads;
+  const int32_t HGn = min(a.tile_heads, a.g - h0);
+  const __bf16* q = (const __bf16*)a.q;
+  __bf16* out = (__bf16*)a.out;
+
+  if (L <= 0) {   // padding request: zero rows
+    for (int e = threadIdx.x; e < kCols * D; e += 256) {
+      const int col = e / D, d = e - col * D;
+      const int i = col / a.tile_heads, j = col - i * a.tile_heads;
+      if (i < Tn && j < HGn) out[((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d] = (__bf16)0.f;
+    }
+    return;
+  }
+
+  const int ni = n / a.tile_heads, nj = n - ni * a.tile_heads;
+  const bool col_ok = ni < Tn && nj < HGn;
+  const int32_t pos = c + it.tok0 + ni;
+  const int32_t kb = it.split * a.split_keys;                   // multiple of 64
+  const int32_t ke = min(c + it.tok0 + Tn, kb + a.split_keys);
+  const int32_t* table_row = a.block_table + (int64_t)it.r * a.stride;
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  const __bf16* kc = (const __bf16*)a.k_cache + (int64_t)hkv * D;
+  const __bf16* vc = (const __bf16*)a.v_cache + (int64_t)hkv * D;
+
+  // Q^T as the B operand: column n, dims 32*kc + 8*G .. +7
+  bf16x8 qf[C::KC];
+  {
+    const __bf16* qrow = q + ((int64_t)(b + it.tok0 + ni) * a.H + hkv * a.g + h0 + nj) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) {
+      if (col_ok) qf[kk] = *(const bf16x8*)(qrow + 32 * kk + 8 * G);
+      else qf[kk] = bf16x8{};
+    }
+  }
+
+  __bf16* vbuf = (__bf16*)smem + w * C::VBUF;
+  f32x4 o[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.f;
+
+  const int32_t nblk_end = (ke + kBlk - 1) / kBlk;               // one past the last block
+  int32_t blk = kb / kBlk + w;
+
+  // registers of the block being loaded
+  bf16x8 kr[C::KC];
+  u32x4 vr[C::VLOADS];
+  auto load_block = [&](int32_t lb) {
+    const int64_t base = (int64_t)table_row[lb] * kBlk;
+    const __bf16* kp = kc + (base + n) * row_elems + 8 * G;
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) kr[kk] = *(const bf16x8*)(kp + 32 * kk);
+#pragma unroll
+    for (int u = 0; u < C::VLOADS; ++u) {
+      const int ci = lane + 64 * u;
+      const int key = ci / C::VPIECES, piece = ci - key * C::VPIECES;
+      vr[u] = *(const u32x4*)(vc + (base + key) * row_elems + 8 * piece);
+    }
+  };
+
+  if (blk < nblk_end) load_block(blk);
+  for (; blk < nblk_end; blk += 4) {
+    // take this block's registers, start the next block's loads
+    bf16x8 kcur[C::KC];
+    u32x4 vcur[C::VLOADS];
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) kcur[kk] = kr[kk];
+#pragma unroll
+    for (int u = 0; u < C::VLOADS; ++u) vcur[u] = vr[u];
+    if (blk + 4 < nblk_end) load_block(blk + 4);
+
+    // S^T = K Q^T
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kk], qf[kk], s, 0, 0, 0);
+
+    // stage V (keys past the split end are zeroed: pool tails may hold NaN)
+    const int32_t key0 = blk * kBlk;
+#pragma unroll
+    for (int u = 0; u < C::VLOADS; ++u) {
+      const int ci = lane + 64 * u;
+      const int key = ci / C::VPIECES, piece = ci - key * C::VPIECES;
+      u32x4 val = vcur[u];
+      if (key0 + key >= ke) val = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(vbuf + key * C::PITCH + 8 * piece) = val;
+    }
+
+    // masked scores in base 2
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t key = key0 + 4 * G + i;
+      sv[i] = (col_ok && key < ke && key <= pos) ? s[i] * a.scale_log2e : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    m = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - m_use);
+    lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    bf16x4 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      phi[i] = (__bf16)p[i];
+      plo[i] = (__bf16)(p[i] - (float)phi[i]);
+    }
+
+    // O^T = alpha * O^T + V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      o[dt] *= alpha;
+      const bf16x4 vt = tr_read(vbuf + (4 * G + (n >> 2)) * C::PITCH + 16 * dt + 4 * (n & 3));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
+    }
+  }
+
+  // combine the four waves: per column max, sum and output
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (G == 0) {
+    sM[w][n] = m;
+    sL[w][n] = lsum;
+  }
+  __syncthreads();   // also: every wave is done with its V buffer
+  float M = kNegInf;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sM[ww][n]);
+  const float M_use = M == kNegInf ? 0.f : M;
+  const float f_own = exp2f(m - M_use);
+  if (w == 0 && G == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) tot += sL[ww][n] * exp2f(sM[ww][n] - M_use);
+    sTot[n] = tot;
+    sMax[n] = M;
+  }
+  float* slab = (float*)smem;                 // [4][16 cols][D]
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slab[(w * kCols + n) * D + 16 * dt + 4 * G + i] = o[dt][i] * f_own;
+  }
+  __syncthreads();
+
+  // each thread finishes 8 consecutive dims of one column
+  constexpr int kPer = 8;
+  for (int e = threadIdx.x * kPer; e < kCols * D; e += 256 * kPer) {
+    const int col = e / D, d = e - col * D;
+    const int i = col / a.tile_heads, j = col - i * a.tile_heads;
+    if (i >= Tn || j >= HGn) continue;
+    float acc[kPer];
+#pragma unroll
+    for (int x = 0; x < kPer; ++x)
+      acc[x] = slab[(0 * kCols + col) * D + d + x] + slab[(1 * kCols + col) * D + d + x] +
+               slab[(2 * kCols + col) * D + d + x] + slab[(3 * kCols + col) * D + d + x];
+    if (it.nsplit == 1) {
+      const float inv = 1.f / sTot[col];
+      bf16x8 r;
+#pragma unroll
+      for (int x = 0; x < kPer; ++x) r[x] = (__bf16)(acc[x] * inv);
+      *(bf16x8*)(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d) = r;
+    } else {
+      const int64_t pi = ((int64_t)blockIdx.x * a.Hkv + hkv) * kCols + col;
+      float4* dst = (float4*)(part.acc + pi * D + d);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      if (d == 0) {
+        part.m[pi] = sMax[col];
+        part.l[pi] = sTot[col];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool small_mfma_supported(int32_t D, int32_t bs) { return bs == kBlk && (D == 64 || D == 128); }
+
+hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s) {
+  if (p.n_small == 0) return hipSuccess;
+  char* w = (char*)ws;
+  const SmallItem* items = (const SmallItem*)(w + p.off_small);
+  Partials part{(float*)(w + p.off_pm), (float*)(w + p.off_pl), (float*)(w + p.off_pacc)};
+  const dim3 grid((unsigned)p.n_small, (unsigned)p.Hkv);
+  if (p.D == 128) hipLaunchKernelGGL(small_tile_mfma<128>, grid, dim3(256), 0, s, a, items, part);
+  else if (p.D == 64) hipLaunchKernelGGL(small_tile_mfma<64>, grid, dim3(256), 0, s, a, items, part);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -134,14 +134,19 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
     for (int j = 0; j < kmax; ++j) {
       const float p = sP[w][j][n];
       const T* vp = vc + slot_of(table_row, k0 + j, a.bs) * row_elems + (int64_t)hkv * D + G * DQ;
+      if constexpr (DQ % 4 == 0) {
 #pragma unroll
-      for (int dd = 0; dd < DQ; dd += 4) {
-        float v4[4];
-        Vec4<T>::load(vp + dd, v4);
-        acc[dd] += p * v4[0];
-        acc[dd + 1] += p * v4[1];
-        acc[dd + 2] += p * v4[2];
-        acc[dd + 3] += p * v4[3];
+        for (int dd = 0; dd < DQ; dd += 4) {
+          float v4[4];
+          Vec4<T>::load(vp + dd, v4);
+          acc[dd] += p * v4[0];
+          acc[dd + 1] += p * v4[1];
+          acc[dd + 2] += p * v4[2];
+          acc[dd + 3] += p * v4[3];
+        }
+      } else {
+#pragma unroll
+        for (int dd = 0; dd < DQ; ++dd) acc[dd] += p * Elem<T>::load(vp + dd);
       }
     }
   }

@@ -1,6 +1,8 @@
 """Runs a batch through the HIP library and through the CPU oracle, for the parity tests."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 from typing import Optional
 
@@ -15,6 +17,14 @@ from tests._util import attention_error, to_np
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def record(entry: dict) -> None:
+    """Append one result line to $PA_PARITY_LOG (if set): a record of each parity check."""
+    path = os.environ.get("PA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
 
 
 def gpu_step(batch, path: int = 0, write: bool = True, out_dtype=None):
@@ -67,5 +77,7 @@ def check_batch(batch, path: int = 0, row_mask: Optional[np.ndarray] = None, lab
     rows = slice(None) if row_mask is None else np.nonzero(row_mask)[0]
     err = attention_error(got[rows], ref64[rows], batch.dtype)
     log(f"[parity] {label or batch.name}: error {err:.3g} x bound")
+    record({"case": label or batch.name, "dtype": batch.dtype, "path": path, "error_x_bound": err,
+            "rows_checked": int(len(got) if row_mask is None else row_mask.sum())})
     assert err <= 1.0, f"{label or batch.name}: error {err:.3g} x the bound"
     return err

@@ -192,6 +192,7 @@ def test_gpu_chunking_invariance(dtype, d):
     for chunk in (8, 33, 64, 4096):
         exact = np.array_equal(outs[chunk], ref)
         H.log(f"[invariance] chunk {chunk}: {'bit-exact' if exact else 'within bound'}")
+        H.record({"case": f"chunking_{dtype}_{chunk}", "bit_exact": bool(exact)})
         # both sides carry float32 rounding; allow twice the single-run bound
         assert attention_error(outs[chunk], ref.astype(np.float64), dtype) <= 2.0
 
@@ -216,6 +217,7 @@ def test_gpu_block_relabelling_and_batch_composition():
                                    for r in b.requests for p in range(r.computed, r.seq_len)], dtype=torch.int64)
     relabelled = _gpu_out(b)
     H.log(f"[invariance] relabelling: {'bit-exact' if np.array_equal(relabelled, ref) else 'differs'}")
+    H.record({"case": "relabelling", "bit_exact": bool(np.array_equal(relabelled, ref))})
     assert np.array_equal(relabelled, ref)
     # the first request alone
     alone = workloads.small_batch([(300, 1)], dtype="bf16", num_heads=16, num_kv_heads=4, head_dim=128, seed=41)
@@ -226,6 +228,7 @@ def test_gpu_block_relabelling_and_batch_composition():
     alone.q, alone.k, alone.v = b.q[:1], b.k[:1], b.v[:1]
     got = _gpu_out(alone)
     H.log(f"[invariance] alone vs batched: {'bit-exact' if np.array_equal(got, ref[:1]) else 'differs'}")
+    H.record({"case": "alone_vs_batched", "bit_exact": bool(np.array_equal(got, ref[:1]))})
     assert attention_error(got, ref[:1].astype(np.float64), "bf16") <= 1.0
 
 
