@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is the whole hot path over one synthetic batch already resident in HBM: the KV
+write of the step's new tokens (slot_mapping scatter) followed by paged varlen attention
+over the flattened batch.  The default workload is the long-context batch (16 decodes at
+32768 tokens plus one 4096-token prefill chunk at position 28672; bf16, 64 query / 8 KV
+heads, head_dim 128, block size 16, 40000-block pool, values N(0,1) with 1% scaled by 10),
+the largest configuration and the one that exercises both the decode and the prefill path.
+
+Prints ONE JSON line.  `value` is the step's attained fraction of the MI355X roofline, in
+percent: max(bytes / 8 TB/s, flops / 2.5 PFLOP/s) over the step's algorithmic work, divided
+by the measured step time.  The decode and prefill halves of the metric are reported beside
+it (decode KV GB/s of the small-tile kernel, prefill TFLOP/s of the prefill kernel), and
+`roofline` describes the dominant kernel, timed with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 matrix cores
+PEAK_F32_TFLOPS = 157.3         # fp32 vector
+METRIC = "paged-attn decode KV GB/s + prefill TFLOP/s, % of MI355X peak"
+KERNEL_SOURCES = {"prefill": "attn_prefill_mfma.hip", "small": "attn_decode_mfma.hip",
+                  "kv_write": "kv_write.hip", "merge": "attn_valu.hip", "plan": "plan.hip"}
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha(kind: str) -> str:
+    path = os.path.join(ROOT, "paged_kv_attention_05_amd", "csrc", KERNEL_SOURCES[kind])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(workload, {}).get(kind)
+    if not entry or entry.get("kernel_sha") != kernel_sha(kind):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_context",
+                    choices=["long_context", "decode_only", "shared_prefix", "mixed_step_bf16",
+                             "mixed_step_f32", "worked_batch"])
+    ap.add_argument("--cpu-prefill-rows", type=int, default=256,
+                    help="prefill rows in the oracle's timed sample (plus every decode row)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        eprint(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+               "this build has no multi-GPU path; the step shards by KV head or by request without "
+               "any exchange, so per-GPU throughput is the single-GPU figure.")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_05_amd as pk
+    import workloads
+    from workloads.accounting import attention_work, write_work
+
+    if not torch.cuda.is_available():
+        eprint("bench.py needs a GPU")
+        return 1
+    pk.load_library()
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    batch = workloads.CONFIGS[args.workload](poison=False)
+    eprint(f"[bench] workload {args.workload}: {batch.description}; generated in {time.time() - t0:.1f}s")
+
+    q, k, v = batch.q.to(dev), batch.k.to(dev), batch.v.to(dev)
+    kc, vc = batch.k_cache.to(dev), batch.v_cache.to(dev)
+    qsl, lens = batch.query_start_loc.to(dev), batch.seq_lens.to(dev)
+    table, slots = batch.block_table.to(dev), batch.slot_mapping.to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = pk.paged_attention_workspace_bytes(batch.num_heads, batch.num_kv_heads, batch.head_dim,
+                                                  batch.block_size, batch.query_start_loc_host,
+                                                  batch.seq_lens_host, q.dtype)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        pk.paged_kv_write(k, v, slots, kc, vc)
+        pk.paged_attention_varlen(q, kc, vc, qsl, lens, table, batch.block_size, batch.scale, out,
+                                  query_start_loc_host=batch.query_start_loc_host,
+                                  seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
+                                  max_seq_len=batch.max_seq_len, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pk.set_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kern = pk.timing_report()
+    pk.set_timing(False)
+    kern_avg = {name: (tot / cnt if cnt else 0.0) for name, (tot, cnt) in kern.items()}
+    eprint(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernels (avg ms): "
+           + ", ".join(f"{n}={t:.4f}" for n, t in kern_avg.items() if t))
+
+    # algorithmic work, split the way the library routes requests
+    g = batch.num_heads // batch.num_kv_heads
+    prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim in (64, 128) \
+        and 128 % g == 0
+    is_pf = [prefill_capable and r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
+    if kern["prefill"][1] == 0:          # the library routed every request to the small tiles
+        is_pf = [False] * len(is_pf)
+    pf_ids = [i for i, f in enumerate(is_pf) if f]
+    dec_ids = [i for i, f in enumerate(is_pf) if not f]
+    w_all = attention_work(batch)
+    w_dec = attention_work(batch, dec_ids) if dec_ids else None
+    w_pf = attention_work(batch, pf_ids) if pf_ids else None
+    w_write = write_work(batch)
+    peak_flops = PEAK_BF16_TFLOPS if batch.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_star = max((w_all["bytes"] + w_write["bytes"]) / (PEAK_HBM_GBPS * 1e9), w_all["flops"] / (peak_flops * 1e12))
+    value = 100.0 * t_star / (ms_per_step * 1e-3)
+
+    decode = None
+    if w_dec is not None and kern_avg["small"] > 0:
+        t = kern_avg["small"] * 1e-3
+        gbps = w_dec["bytes"] / t / 1e9
+        decode = {"kernel": "small_tile_mfma" if batch.dtype == "bf16" else "small_tile_valu",
+                  "avg_ms": kern_avg["small"], "merge_avg_ms": kern_avg["merge"],
+                  "algorithmic_bytes": w_dec["bytes"], "kv_bytes": w_dec["kv_bytes"],
+                  "kv_gbps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS,
+                  "kv_gbps_incl_merge": w_dec["bytes"] / ((kern_avg["small"] + kern_avg["merge"]) * 1e-3) / 1e9}
+    prefill = None
+    if w_pf is not None and kern_avg["prefill"] > 0:
+        t = kern_avg["prefill"] * 1e-3
+        tf = w_pf["flops"] / t / 1e12
+        prefill = {"kernel": "prefill_tile_mfma", "avg_ms": kern_avg["prefill"], "algorithmic_flops": w_pf["flops"],
+                   "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
+
+    # dominant kernel: the one taking the most time per step
+    dom = max(("prefill", "small", "kv_write"), key=lambda n: kern_avg[n])
+    if dom == "prefill":
+        roof = {"kernel": "prefill_tile_mfma", "bound": "mfma", "achieved": prefill["tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": prefill["frac_mfma"],
+                "algorithmic_per_launch": w_pf["flops"], "avg_launch_ms": kern_avg["prefill"]}
+    elif dom == "small":
+        roof = {"kernel": decode["kernel"], "bound": "hbm", "achieved": decode["kv_gbps"], "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": decode["frac_hbm"], "algorithmic_per_launch": w_dec["bytes"],
+                "avg_launch_ms": kern_avg["small"]}
+    else:
+        gb = w_write["bytes"] / (kern_avg["kv_write"] * 1e-3) / 1e9
+        roof = {"kernel": "kv_copy16", "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gb / PEAK_HBM_GBPS, "algorithmic_per_launch": w_write["bytes"],
+                "avg_launch_ms": kern_avg["kv_write"]}
+    roof["traffic"] = measured_traffic(dom, args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's sample is chosen by request shape: every row of requests whose rows times
+        # grouped heads fit 16 columns (decodes), and a spread of rows from the longer chunks
+        chunk = [r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
+        cpu = cpu_baseline(batch, args.cpu_prefill_rows, [i for i, f in enumerate(chunk) if not f],
+                           [i for i, f in enumerate(chunk) if f], peak_flops)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "% of MI355X peak", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": batch.dtype, "data": "synthetic",
+        "config": {"workload": batch.name, "description": batch.description, "num_tokens": batch.num_tokens,
+                   "num_reqs": batch.num_reqs, "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
+                   "head_dim": batch.head_dim, "block_size": batch.block_size, "pool_blocks": batch.num_blocks,
+                   "parallelism": "single-gpu"},
+        "step_roofline_ms": t_star * 1e3,
+        "step_algorithmic": {"bytes": w_all["bytes"] + w_write["bytes"], "flops": w_all["flops"]},
+        "decode": decode, "prefill": prefill,
+        "kv_write": {"avg_ms": kern_avg["kv_write"], "bytes": w_write["bytes"],
+                     "gbps": w_write["bytes"] / (kern_avg["kv_write"] * 1e-3) / 1e9 if kern_avg["kv_write"] else None},
+        "kernels_avg_ms": kern_avg,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops):
+    """The oracle (float64 C, OpenMP) timed on the host on a bounded sample of the same step:
+    the full KV write, then attention for every decode row and `n_prefill_rows` prefill rows
+    spread evenly over the chunk.  Reported in the metric's unit (the sample's roofline time
+    at MI355X peak over the oracle's time), with the raw rates beside it."""
+    import numpy as np
+
+    import oracle
+    from tests._util import to_np
+
+    mask = np.zeros(batch.num_tokens, np.uint8)
+    flops = 0.0
+    touched = set()
+    qsl = batch.query_start_loc_host
+    for r in dec_ids:
+        mask[qsl[r]:qsl[r + 1]] = 1
+    pf_rows = [i for r in pf_ids for i in range(qsl[r], qsl[r + 1])]
+    if pf_rows and n_prefill_rows > 0:
+        pick = np.linspace(0, len(pf_rows) - 1, min(n_prefill_rows, len(pf_rows))).round().astype(int)
+        mask[np.array(pf_rows)[pick]] = 1
+    for r, req in enumerate(batch.requests):
+        rows = np.nonzero(mask[qsl[r]:qsl[r + 1]])[0]
+        if len(rows):
+            touched.add(r)
+            flops += 4.0 * batch.num_heads * batch.head_dim * float(np.sum(req.computed + rows + 1))
+    from workloads.accounting import attention_work
+    kv = attention_work(batch, sorted(touched))["kv_bytes"] if touched else 0.0
+    nbytes = kv + int(mask.sum()) * batch.num_heads * batch.head_dim * 2 * (2 if batch.dtype == "bf16" else 4)
+    kc, vc = to_np(batch.k_cache).copy(), to_np(batch.v_cache).copy()
+    q, k, v = to_np(batch.q), to_np(batch.k), to_np(batch.v)
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    oracle.kv_write(k, v, batch.slot_mapping.numpy(), kc, vc, batch.dtype, batch.dtype)
+    oracle.paged_attention(q, kc, vc, batch.query_start_loc.numpy(), batch.seq_lens.numpy(),
+                           batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=mask)
+    secs = time.perf_counter() - t0
+    t_star = max(nbytes / (PEAK_HBM_GBPS * 1e9), flops / (peak_flops * 1e12))
+    eprint(f"[bench] oracle sample: {int(mask.sum())} rows in {secs:.2f}s on {cores} threads")
+    return {"value": 100.0 * t_star / secs, "unit": "% of MI355X peak", "cores": cores, "kind": "oracle",
+            "seconds": secs, "flops_per_s": flops / secs, "kv_bytes_per_s": kv / secs,
+            "sample": f"KV write of all {batch.num_tokens} tokens + attention of {int(mask.sum())} of "
+                      f"{batch.num_tokens} rows (every decode row, {min(n_prefill_rows, len(pf_rows))} prefill "
+                      f"rows evenly spaced), {batch.name}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

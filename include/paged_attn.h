@@ -100,9 +100,10 @@ size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int
  * cores with float32 accumulation; probabilities are rounded to bf16 for the PV product);
  * out is rounded to nearest-even.
  *
- * Supported: head_dim a multiple of 8, 8..256; block_size >= 1 (the bf16 matrix-core
- * paths need block_size 16 and head_dim 64 or 128; other shapes use the vector path);
- * num_heads % num_kv_heads == 0.  workspace must hold paged_attention_workspace_bytes().
+ * Supported: head_dim in {8, 16, 32, 48, 64, 96, 128, 256}; block_size >= 1 (the bf16
+ * matrix-core paths need block_size 16 and head_dim 64 or 128; other shapes use the
+ * vector path); num_heads % num_kv_heads == 0; q, out, caches and workspace 16-byte
+ * aligned.  workspace must hold paged_attention_workspace_bytes().
  *
  * Preconditions not checked (unless debug checks are on): block ids in range; the K/V
  * of every visible position has been written.
@@ -132,6 +133,23 @@ const char* paged_attn_last_error(void);
  * 1 = vector-ALU tile kernel for every request.  Applies to later calls on this thread.
  */
 void paged_attn_set_path(int32_t path);
+
+/*
+ * Kernel timing (measurement only).  While enabled, every launch the library makes on this
+ * thread is bracketed by a pair of HIP events recorded on the caller's stream.
+ * paged_attn_timing_report waits for those events, writes per-kind sums of the elapsed
+ * milliseconds (total_ms[kind]) and launch counts (count[kind]) for kinds
+ * 0 = KV write, 1 = work planner, 2 = prefill tile kernel, 3 = small-tile kernel,
+ * 4 = split merge, and forgets the recorded launches.  Returns the number of kinds written
+ * (min(n_kinds, 5)), or a negative PA_ERR_* code.
+ */
+#define PA_KIND_KV_WRITE 0
+#define PA_KIND_PLAN 1
+#define PA_KIND_PREFILL 2
+#define PA_KIND_SMALL 3
+#define PA_KIND_MERGE 4
+void paged_attn_set_timing(int32_t enable);
+int paged_attn_timing_report(double* total_ms, int32_t* count, int32_t n_kinds);
 
 #ifdef __cplusplus
 }

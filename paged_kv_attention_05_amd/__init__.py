@@ -25,7 +25,9 @@ PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
           -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
 EXPORTS = ["paged_kv_write", "paged_attention_varlen", "paged_attention_workspace_bytes",
-           "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path"]
+           "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
+           "paged_attn_set_timing", "paged_attn_timing_report"]
+KINDS = ["kv_write", "plan", "prefill", "small", "merge"]
 
 _lib = None
 
@@ -58,6 +60,10 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_set_debug_checks.argtypes = [I32]
     lib.paged_attn_set_path.restype = None
     lib.paged_attn_set_path.argtypes = [I32]
+    lib.paged_attn_set_timing.restype = None
+    lib.paged_attn_set_timing.argtypes = [I32]
+    lib.paged_attn_timing_report.restype = ctypes.c_int
+    lib.paged_attn_timing_report.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32), I32]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -95,6 +101,22 @@ def set_debug_checks(enable: bool) -> None:
 def set_path(path: int) -> None:
     """0: automatic kernel choice; 1: vector-ALU tile kernel for every request."""
     load_library().paged_attn_set_path(int(path))
+
+
+def set_timing(enable: bool) -> None:
+    """Bracket every library launch on this thread with HIP events (measurement only)."""
+    load_library().paged_attn_set_timing(1 if enable else 0)
+
+
+def timing_report() -> dict:
+    """{kind: (total_ms, launches)} over the launches recorded since timing was enabled."""
+    lib = load_library()
+    tot = (ctypes.c_double * len(KINDS))()
+    cnt = (ctypes.c_int32 * len(KINDS))()
+    rc = lib.paged_attn_timing_report(tot, cnt, len(KINDS))
+    if rc < 0:
+        _check(rc)
+    return {KINDS[i]: (float(tot[i]), int(cnt[i])) for i in range(len(KINDS))}
 
 
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,

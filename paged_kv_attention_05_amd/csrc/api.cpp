@@ -24,6 +24,34 @@ namespace {
 thread_local std::string g_last_error;
 thread_local int g_debug_checks = 0;
 thread_local int g_path = 0;
+thread_local int g_timing = 0;
+
+// Kernel timing: event pairs recorded around each launch while timing is on.
+struct TimedLaunch {
+  hipEvent_t start, stop;
+  int kind;
+};
+thread_local std::vector<TimedLaunch> g_events;   // created once, reused
+thread_local size_t g_events_used = 0;
+constexpr int kKinds = 5;
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  if (!g_timing) return launch();
+  if (g_events_used == g_events.size()) {
+    TimedLaunch t{};
+    if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess)
+      return hipErrorOutOfMemory;
+    g_events.push_back(t);
+  }
+  TimedLaunch& t = g_events[g_events_used++];
+  t.kind = kind;
+  hipError_t e = hipEventRecord(t.start, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(t.stop, s);
+}
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
@@ -117,6 +145,30 @@ void paged_attn_set_debug_checks(int32_t enable) { g_debug_checks = enable != 0;
 
 void paged_attn_set_path(int32_t path) { g_path = path; }
 
+void paged_attn_set_timing(int32_t enable) {
+  g_timing = enable != 0;
+  g_events_used = 0;
+}
+
+int paged_attn_timing_report(double* total_ms, int32_t* count, int32_t n_kinds) {
+  g_last_error.clear();
+  if (!total_ms || !count) return fail(PA_ERR_NULL, "null pointer argument");
+  const int k = std::min<int>(std::max<int>(n_kinds, 0), kKinds);
+  for (int i = 0; i < k; ++i) { total_ms[i] = 0.0; count[i] = 0; }
+  for (size_t i = 0; i < g_events_used; ++i) {
+    TimedLaunch& t = g_events[i];
+    if (hipEventSynchronize(t.stop) != hipSuccess) return fail(PA_ERR_LAUNCH, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) return fail(PA_ERR_LAUNCH, "event timing failed");
+    if (t.kind < k) {
+      total_ms[t.kind] += ms;
+      count[t.kind] += 1;
+    }
+  }
+  g_events_used = 0;
+  return k;
+}
+
 int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
                    void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                    int64_t num_slots, int32_t in_dtype, int32_t cache_dtype, hipStream_t stream) {
@@ -142,8 +194,10 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, vo
         return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] repeats a slot");
     }
   }
-  const hipError_t e = pa::launch_kv_write(k, v, slot_mapping, k_cache, v_cache, num_tokens, (int32_t)row,
-                                           num_slots, in_dtype, cache_dtype, stream);
+  const hipError_t e = timed(PA_KIND_KV_WRITE, stream, [&] {
+    return pa::launch_kv_write(k, v, slot_mapping, k_cache, v_cache, num_tokens, (int32_t)row, num_slots,
+                               in_dtype, cache_dtype, stream);
+  });
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("kv write launch: ") + hipGetErrorString(e));
   return PA_OK;
 }
@@ -209,12 +263,16 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
   a.split_keys = p.split_keys;
   a.scale_log2e = scale * 1.4426950408889634f;
 
-  hipError_t e = pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream);
-  if (e == hipSuccess && p.n_pf > 0) e = pa::launch_prefill_mfma(p, a, workspace, stream);
+  hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
+  if (e == hipSuccess && p.n_pf > 0)
+    e = timed(PA_KIND_PREFILL, stream, [&] { return pa::launch_prefill_mfma(p, a, workspace, stream); });
   if (e == hipSuccess && p.n_small > 0)
-    e = p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)
-                           : pa::launch_small_valu(p, a, workspace, dtype, stream);
-  if (e == hipSuccess && p.n_merge > 0) e = pa::launch_merge(p, a, workspace, dtype, stream);
+    e = timed(PA_KIND_SMALL, stream, [&] {
+      return p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)
+                                : pa::launch_small_valu(p, a, workspace, dtype, stream);
+    });
+  if (e == hipSuccess && p.n_merge > 0)
+    e = timed(PA_KIND_MERGE, stream, [&] { return pa::launch_merge(p, a, workspace, dtype, stream); });
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("attention launch: ") + hipGetErrorString(e));
   return PA_OK;
 }

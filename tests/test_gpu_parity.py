@@ -120,13 +120,19 @@ EDGE = [
     ("long_decode_f32", [(5000, 1)], 4, 2, 64, 16, "f32"),
     ("block_boundaries", [(15, 1), (16, 1), (31, 2), (32, 16), (47, 17)], 8, 2, 128, 16, "bf16"),
     ("chunk_ragged_tail", [(1000, 131), (0, 200)], 16, 4, 128, 16, "bf16"),
+    ("prefill_g8_d64", [(500, 300), (0, 77), (2, 1)], 64, 8, 64, 16, "bf16"),
+    ("prefill_g2", [(33, 200), (64, 64)], 8, 4, 128, 16, "bf16"),
+    ("prefill_g1_long_context", [(3000, 129)], 8, 8, 128, 16, "bf16"),
+    ("prefill_g16_d64", [(100, 9), (0, 3)], 32, 2, 64, 16, "bf16"),
+    ("prefill_outliers", [(700, 150), (90, 1)], 32, 8, 128, 16, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("name,specs,h,hkv,d,bs,dtype", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     b = workloads.small_batch(specs, dtype=dtype, num_heads=h, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                              seed=zlib.crc32(name.encode()) % 1000)
+                              seed=zlib.crc32(name.encode()) % 1000,
+                              outlier_p=0.01 if "outliers" in name else 0.0)
     H.check_batch(b, label=name)
 
 
