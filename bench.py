@@ -69,6 +69,9 @@ def main() -> int:
     ap.add_argument("--cpu-prefill-rows", type=int, default=256,
                     help="prefill rows in the oracle's timed sample (plus every decode row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, copy this many MiB device-to-device once: a plain copy "
+                         "of known size whose HBM counters scale the kernels' counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +114,16 @@ def main() -> int:
                                   query_start_loc_host=batch.query_start_loc_host,
                                   seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
                                   max_seq_len=batch.max_seq_len, workspace=ws)
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"[bench] calibration copy: {nbytes} bytes read, {nbytes} bytes written")
+        del src, dst
 
     for _ in range(args.warmup):
         step()

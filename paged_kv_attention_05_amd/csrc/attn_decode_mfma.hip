@@ -22,7 +22,10 @@
 //                                           LDS transpose read (ds_read_tr16_b64).
 // P is split into bf16 high and low parts (two products) so the probabilities keep ~16
 // bits: cheap here, since the path is bound by HBM, not by the matrix cores.
-// The next block's K and V are loaded into registers while the current one is computed.
+// K goes from HBM straight into registers (two sets, ping-pong) and V straight into a
+// per-wave LDS buffer (gfx950 direct loads, two buffers), so the next block is in flight
+// while the current one is computed.  Keys past the split end are read from the last
+// visible key instead (finite data, masked), so no NaN from an unwritten slot enters.
 #include "pa_internal.h"
 
 namespace pa {
@@ -41,31 +44,44 @@ template <int D>
 struct DecodeCfg {
   static constexpr int KC = D / 32;           // k-chunks of the QK^T product
   static constexpr int DT = D / 16;           // 16-wide d tiles of the PV product
-  static constexpr int PITCH = D + 16;        // LDS row pitch (elements): conflict-free transpose reads
-  static constexpr int VPIECES = D / 8;       // 16-byte pieces per V row
-  static constexpr int VLOADS = kBlk * VPIECES / 64;   // 16-byte loads per lane per V block
-  static constexpr int VBUF = kBlk * PITCH;   // elements of one wave's V buffer
+  static constexpr int ROW = D * 2;           // bytes of one key row in LDS
+  static constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROW;      // rows one direct-load instruction fills
+  static constexpr int VLOADS = kBlk / RPI;   // direct-load instructions per wave per block
+  static constexpr int VBUF = kBlk * ROW;     // bytes of one wave's V buffer
 };
 
-__device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
+// Chunk swizzle of a V row in LDS (chunk c of row r sits at slot c ^ vswz(r)): makes the
+// transpose reads of a 16-key block (rows 0..7 x two adjacent chunks per half-wave) hit
+// 16 distinct 16-byte slots of the 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
   return __builtin_bit_cast(bf16x4, r);
 }
 
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
+__global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
                                                        Partials part) {
   using C = DecodeCfg<D>;
-  // V staging (per wave) and, after the key loop, the per-wave output slabs.
-  constexpr int kVBytes = 4 * C::VBUF * 2;
+  // per wave: two V buffers; after the key loop the same bytes hold the per-wave output slabs
+  constexpr int kVBytes = 4 * 2 * C::VBUF;
   constexpr int kSlabBytes = 4 * kCols * D * 4;
-  __shared__ __align__(16) unsigned char smem[kVBytes > kSlabBytes ? kVBytes : kSlabBytes];
+  __shared__ __align__(1024) unsigned char smem[kVBytes > kSlabBytes ? kVBytes : kSlabBytes];
   __shared__ float sM[4][kCols], sL[4][kCols], sTot[kCols], sMax[kCols];
 
   const SmallItem it = items[blockIdx.x];
   const int hkv = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave id: uniform
   const int n = lane & 15, G = lane >> 4;
   const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b, L = a.seq_lens[it.r], c = L - t;
   const int32_t Tn = min(a.tile_tokens, t - it.tok0);
@@ -93,86 +109,70 @@ __global__ __launch_bounds__(256) void small_tile_mfma(AttnArgs a, const SmallIt
   const __bf16* kc = (const __bf16*)a.k_cache + (int64_t)hkv * D;
   const __bf16* vc = (const __bf16*)a.v_cache + (int64_t)hkv * D;
 
-  // Q^T as the B operand: column n, dims 32*kc + 8*G .. +7
+  // Q^T as the B operand: column n, dims 32*kk + 8*G .. +7; a negative scale becomes -q
+  const float sl = fmaxf(fabsf(a.scale_log2e), 1e-30f);
+  const uint32_t qsign = a.scale_log2e < 0.f ? 0x80008000u : 0u;
   bf16x8 qf[C::KC];
   {
     const __bf16* qrow = q + ((int64_t)(b + it.tok0 + ni) * a.H + hkv * a.g + h0 + nj) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
-      if (col_ok) qf[kk] = *(const bf16x8*)(qrow + 32 * kk + 8 * G);
-      else qf[kk] = bf16x8{};
+      u32x4 v = col_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * G) : u32x4{0u, 0u, 0u, 0u};
+      v ^= qsign;
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  __bf16* vbuf = (__bf16*)smem + w * C::VBUF;
+  unsigned char* vbuf0 = smem + w * 2 * C::VBUF;
   f32x4 o[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
 
   const int32_t nblk_end = (ke + kBlk - 1) / kBlk;               // one past the last block
-  int32_t blk = kb / kBlk + w;
-
-  // registers of the block being loaded
-  bf16x8 kr[C::KC];
-  u32x4 vr[C::VLOADS];
-  auto load_block = [&](int32_t lb) {
-    const int64_t base = (int64_t)table_row[lb] * kBlk;
-    const __bf16* kp = kc + (base + n) * row_elems + 8 * G;
+  const int32_t blk0 = kb / kBlk + w;
+  // key rows past the split end are read from key ke-1 instead: finite data, masked out
+  auto slot_of_key = [&](int32_t key) -> int64_t {
+    key = key < ke ? key : ke - 1;
+    return (int64_t)table_row[key >> 4] * kBlk + (key & 15);
+  };
+  // K block straight into the A operand (lane: key n, dims 8G + 32kk .. +7)
+  auto load_k = [&](int32_t lb, bf16x8* kr) {
+    const __bf16* kp = kc + slot_of_key(lb * kBlk + n) * row_elems + 8 * G;
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) kr[kk] = *(const bf16x8*)(kp + 32 * kk);
+  };
+  // V block straight into this wave's LDS buffer: instruction u fills rows RPI*u .. +RPI-1;
+  // lane l takes row RPI*u + l / CHUNKS, slot l % CHUNKS, holding chunk slot ^ vswz(row)
+  auto load_v = [&](int32_t lb, unsigned char* dst) {
 #pragma unroll
     for (int u = 0; u < C::VLOADS; ++u) {
-      const int ci = lane + 64 * u;
-      const int key = ci / C::VPIECES, piece = ci - key * C::VPIECES;
-      vr[u] = *(const u32x4*)(vc + (base + key) * row_elems + 8 * piece);
+      const int r = C::RPI * u + lane / C::CHUNKS;
+      const int chunk = (lane % C::CHUNKS) ^ vswz<D>(r);
+      load_lds16(vc + slot_of_key(lb * kBlk + r) * row_elems + 8 * chunk, dst + u * 1024);
     }
   };
 
-  if (blk < nblk_end) load_block(blk);
-  for (; blk < nblk_end; blk += 4) {
-    // take this block's registers, start the next block's loads
-    bf16x8 kcur[C::KC];
-    u32x4 vcur[C::VLOADS];
-#pragma unroll
-    for (int kk = 0; kk < C::KC; ++kk) kcur[kk] = kr[kk];
-#pragma unroll
-    for (int u = 0; u < C::VLOADS; ++u) vcur[u] = vr[u];
-    if (blk + 4 < nblk_end) load_block(blk + 4);
-
+  auto compute = [&](int32_t lb, const bf16x8* kcur, const unsigned char* vb) {
     // S^T = K Q^T
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kk], qf[kk], s, 0, 0, 0);
-
-    // stage V (keys past the split end are zeroed: pool tails may hold NaN)
-    const int32_t key0 = blk * kBlk;
-#pragma unroll
-    for (int u = 0; u < C::VLOADS; ++u) {
-      const int ci = lane + 64 * u;
-      const int key = ci / C::VPIECES, piece = ci - key * C::VPIECES;
-      u32x4 val = vcur[u];
-      if (key0 + key >= ke) val = u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(vbuf + key * C::PITCH + 8 * piece) = val;
-    }
-
-    // masked scores in base 2
+    // masked scores, running max (base 2)
+    const int32_t key0 = lb * kBlk + 4 * G;
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t key = key0 + 4 * G + i;
-      sv[i] = (col_ok && key < ke && key <= pos) ? s[i] * a.scale_log2e : kNegInf;
-    }
+    for (int i = 0; i < 4; ++i) sv[i] = (col_ok && key0 + i < ke && key0 + i <= pos) ? s[i] : kNegInf;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
+    const float m_new = fmaxf(m, mx * sl);
+    const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;   // m may be -inf
     m = m_new;
+    const float m_use = m == kNegInf ? 0.f : m;
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - m_use);
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl, -m_use));
     lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
     bf16x4 phi, plo;
 #pragma unroll
@@ -180,15 +180,45 @@ __global__ __launch_bounds__(256) void small_tile_mfma(AttnArgs a, const SmallIt
       phi[i] = (__bf16)p[i];
       plo[i] = (__bf16)(p[i] - (float)phi[i]);
     }
-
     // O^T = alpha * O^T + V^T P^T
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       o[dt] *= alpha;
-      const bf16x4 vt = tr_read(vbuf + (4 * G + (n >> 2)) * C::PITCH + 16 * dt + 4 * (n & 3));
+      const int r = 4 * G + (n >> 2);
+      const int chunk = 2 * dt + ((n & 3) >> 1);
+      const bf16x4 vt = tr_read(vb + r * C::ROW + 16 * (chunk ^ vswz<D>(r)) + 8 * (n & 1));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
     }
+  };
+
+  // blocks blk0, blk0 + 4, ... of this wave, two at a time: K ping-pongs between two register
+  // sets, V between two LDS buffers; the next block's loads are in flight during each compute
+  bf16x8 kA[C::KC], kB[C::KC];
+  if (blk0 < nblk_end) {
+    load_k(blk0, kA);
+    load_v(blk0, vbuf0);
+  }
+  for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
+    const bool has1 = lb + 4 < nblk_end;
+    if (has1) {
+      load_k(lb + 4, kB);
+      load_v(lb + 4, vbuf0 + C::VBUF);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute(lb, kA, vbuf0);
+    if (!has1) break;
+    const bool has2 = lb + 8 < nblk_end;
+    if (has2) {
+      load_k(lb + 8, kA);
+      load_v(lb + 8, vbuf0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb+4 landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute(lb + 4, kB, vbuf0 + C::VBUF);
   }
 
   // combine the four waves: per column max, sum and output
@@ -198,16 +228,16 @@ __global__ __launch_bounds__(256) void small_tile_mfma(AttnArgs a, const SmallIt
     sM[w][n] = m;
     sL[w][n] = lsum;
   }
-  __syncthreads();   // also: every wave is done with its V buffer
+  __syncthreads();   // also: every wave is done with its V buffers
   float M = kNegInf;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sM[ww][n]);
   const float M_use = M == kNegInf ? 0.f : M;
-  const float f_own = exp2f(m - M_use);
+  const float f_own = __builtin_amdgcn_exp2f(m - M_use);
   if (w == 0 && G == 0) {
     float tot = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) tot += sL[ww][n] * exp2f(sM[ww][n] - M_use);
+    for (int ww = 0; ww < 4; ++ww) tot += sL[ww][n] * __builtin_amdgcn_exp2f(sM[ww][n] - M_use);
     sTot[n] = tot;
     sMax[n] = M;
   }

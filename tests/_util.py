@@ -94,3 +94,14 @@ def attention_error(got: np.ndarray, ref64: np.ndarray, dtype: str) -> float:
     else:
         bound = 2e-2 + 0.5 * bf16_ulp(ref64)
     return float((diff / bound).max())
+
+
+def rounding_excess(got: np.ndarray, ref64: np.ndarray) -> float:
+    """bfloat16 outputs: the largest error beyond half a bf16 ulp of the reference (the part
+    the output rounding cannot explain), as a fraction of 2e-2.  Shows how much of the
+    absolute budget the kernel's arithmetic itself uses."""
+    got = np.asarray(got, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    ex = np.abs(got - ref64) - 0.5 * bf16_ulp(ref64)
+    return float(max(0.0, ex.max()) / 2e-2)

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import paged_kv_attention_05_amd as pk
-from tests._util import attention_error, to_np
+from tests._util import attention_error, rounding_excess, to_np
 
 
 def log(msg: str) -> None:
@@ -77,7 +77,10 @@ def check_batch(batch, path: int = 0, row_mask: Optional[np.ndarray] = None, lab
     rows = slice(None) if row_mask is None else np.nonzero(row_mask)[0]
     err = attention_error(got[rows], ref64[rows], batch.dtype)
     log(f"[parity] {label or batch.name}: error {err:.3g} x bound")
-    record({"case": label or batch.name, "dtype": batch.dtype, "path": path, "error_x_bound": err,
-            "rows_checked": int(len(got) if row_mask is None else row_mask.sum())})
+    entry = {"case": label or batch.name, "dtype": batch.dtype, "path": path, "error_x_bound": err,
+             "rows_checked": int(len(got) if row_mask is None else row_mask.sum())}
+    if batch.dtype == "bf16":
+        entry["excess_over_rounding_x_2e-2"] = rounding_excess(got[rows], ref64[rows])
+    record(entry)
     assert err <= 1.0, f"{label or batch.name}: error {err:.3g} x the bound"
     return err
