@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   __shared__ __align__(1024) unsigned char smem[kVBytes > kSlabBytes ? kVBytes : kSlabBytes];
   __shared__ float sM[4][kCols], sL[4][kCols], sTot[kCols], sMax[kCols];
 
-  const SmallItem it = items[blockIdx.x];
+  const int32_t item = blockIdx.x;
   const int hkv = blockIdx.y;
+  const SmallItem it = items[item];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave id: uniform
   const int n = lane & 15, G = lane >> 4;
   const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b, L = a.seq_lens[it.r], c = L - t;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
       for (int x = 0; x < kPer; ++x) r[x] = (__bf16)(acc[x] * inv);
       *(bf16x8*)(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d) = r;
     } else {
-      const int64_t pi = ((int64_t)blockIdx.x * a.Hkv + hkv) * kCols + col;
+      const int64_t pi = ((int64_t)item * a.Hkv + hkv) * kCols + col;
       float4* dst = (float4*)(part.acc + pi * D + d);
       dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);

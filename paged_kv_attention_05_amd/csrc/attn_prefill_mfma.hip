@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   }
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 
 }  // namespace
 

@@ -203,33 +203,38 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
 }
 
 // Combine the splits of a small tile: M = max m_s, out = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s.
+// One thread per (column, dim) output; a workgroup takes 256 / D columns of one tile and KV
+// head (blockIdx.y picks the column group), so even a handful of long decodes spreads over
+// many compute units.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_splits(AttnArgs a, const MergeItem* __restrict__ items,
                                                     Partials part) {
-  const MergeItem it = items[blockIdx.x];
-  const int hkv = blockIdx.y;
   const int D = a.D;
+  const int cols_per_wg = 256 / D;
+  const int hkv = blockIdx.x % a.Hkv;
+  const MergeItem it = items[blockIdx.x / a.Hkv];
+  const int col = blockIdx.y * cols_per_wg + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (col >= kCols || threadIdx.x >= cols_per_wg * D) return;
   const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b;
   const int32_t Tn = min(a.tile_tokens, t - it.tok0);
   const int32_t h0 = it.hsub * a.tile_heads;
   const int32_t HGn = min(a.tile_heads, a.g - h0);
-  T* out = (T*)a.out;
-  for (int e = threadIdx.x; e < kCols * D; e += 256) {
-    const int col = e / D, d = e - col * D;
-    const int i = col / a.tile_heads, j = col - i * a.tile_heads;
-    if (i >= Tn || j >= HGn) continue;
-    float M = kNegInf;
-    for (int s = 0; s < it.nsplit; ++s)
-      M = fmaxf(M, part.m[((int64_t)(it.first + s) * a.Hkv + hkv) * kCols + col]);
-    float lt = 0.f, o = 0.f;
-    for (int s = 0; s < it.nsplit; ++s) {
-      const int64_t pi = ((int64_t)(it.first + s) * a.Hkv + hkv) * kCols + col;
-      const float f = exp2f(part.m[pi] - M);
-      lt += f * part.l[pi];
-      o += f * part.acc[pi * D + d];
-    }
-    Elem<T>::store(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d, o / lt);
+  const int i = col / a.tile_heads, j = col - i * a.tile_heads;
+  if (i >= Tn || j >= HGn) return;
+  const int64_t base = ((int64_t)it.first * a.Hkv + hkv) * kCols + col;
+  const int64_t step = (int64_t)a.Hkv * kCols;                  // next split of the same column
+  float M = kNegInf;
+  for (int s = 0; s < it.nsplit; ++s) M = fmaxf(M, part.m[base + s * step]);
+  float lt = 0.f, o = 0.f;
+  for (int s = 0; s < it.nsplit; ++s) {
+    const int64_t pi = base + s * step;
+    const float f = exp2f(part.m[pi] - M);
+    lt += f * part.l[pi];
+    o += f * part.acc[pi * D + d];
   }
+  T* out = (T*)a.out;
+  Elem<T>::store(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d, o / lt);
 }
 
 template <typename T>
@@ -267,7 +272,8 @@ hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtyp
   char* w = (char*)ws;
   const MergeItem* items = (const MergeItem*)(w + p.off_merge);
   Partials part{(float*)(w + p.off_pm), (float*)(w + p.off_pl), (float*)(w + p.off_pacc)};
-  const dim3 grid((unsigned)p.n_merge, (unsigned)p.Hkv);
+  const int cols_per_wg = 256 / p.D;
+  const dim3 grid((unsigned)(p.n_merge * p.Hkv), (unsigned)((kCols + cols_per_wg - 1) / cols_per_wg));
   if (dtype == 0) hipLaunchKernelGGL(merge_splits<float>, grid, dim3(256), 0, s, a, items, part);
   else hipLaunchKernelGGL(merge_splits<uint16_t>, grid, dim3(256), 0, s, a, items, part);
   return hipGetLastError();
