@@ -81,10 +81,18 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
 
   const int32_t item = blockIdx.x;
   const int hkv = blockIdx.y;
-  const SmallItem it = items[item];
+  SmallItem it = items[item];
+  // the item is the same for the whole workgroup: scalar registers, scalar loop bounds
+  it.r = __builtin_amdgcn_readfirstlane(it.r);
+  it.tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
+  it.hsub = __builtin_amdgcn_readfirstlane(it.hsub);
+  it.split = __builtin_amdgcn_readfirstlane(it.split);
+  it.nsplit = __builtin_amdgcn_readfirstlane(it.nsplit);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave id: uniform
   const int n = lane & 15, G = lane >> 4;
-  const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b, L = a.seq_lens[it.r], c = L - t;
+  const int32_t b = __builtin_amdgcn_readfirstlane(a.qsl[it.r]);
+  const int32_t t = __builtin_amdgcn_readfirstlane(a.qsl[it.r + 1]) - b;
+  const int32_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[it.r]), c = L - t;
   const int32_t Tn = min(a.tile_tokens, t - it.tok0);
   const int32_t h0 = it.hsub * a.tile_heads;
   const int32_t HGn = min(a.tile_heads, a.g - h0);

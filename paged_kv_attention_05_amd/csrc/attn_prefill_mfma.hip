@@ -97,11 +97,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave id: uniform
   const int n = lane & 31, h = lane >> 5;
   const int BQ = ROWS / a.g;                                  // tokens per tile
-  const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b, L = a.seq_lens[it.r], c = L - t;
-  const int32_t tok0 = it.tok0;
+  // request metadata is the same for the whole workgroup: keep it in scalar registers so
+  // every tile bound and branch below is scalar
+  const int32_t r_id = __builtin_amdgcn_readfirstlane(it.r);
+  const int32_t b = __builtin_amdgcn_readfirstlane(a.qsl[r_id]);
+  const int32_t t = __builtin_amdgcn_readfirstlane(a.qsl[r_id + 1]) - b;
+  const int32_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[r_id]);
+  const int32_t c = L - t;
+  const int32_t tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
   const int32_t Tn = min(BQ, t - tok0);
   const int32_t kend = c + tok0 + Tn;                         // one past the last visible key
-  const int32_t* table_row = a.block_table + (int64_t)it.r * a.stride;
+  const int32_t* table_row = a.block_table + (int64_t)r_id * a.stride;
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const __bf16* kc = (const __bf16*)a.k_cache + (int64_t)hkv * D;
   const __bf16* vc = (const __bf16*)a.v_cache + (int64_t)hkv * D;
