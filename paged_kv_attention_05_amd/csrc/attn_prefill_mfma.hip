@@ -179,15 +179,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int G = lane >> 4, i16 = lane & 15;
 
   // S^T of one K tile (keys 64j .. 64j+63, two halves of 32 keys)
+  // (the two halves alternate, so consecutive matrix instructions are independent)
   auto qk = [&](const unsigned char* Ks, f32x16* s) {
+    const int sw = swz(n);                                  // swz(32 + n) == swz(n)
 #pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const int r = 32 * sh + n;
-      const unsigned char* krow = Ks + r * C::ROW;
-      const int sw = swz(r);
+    for (int kk = 0; kk < C::KC; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < C::KC; ++kk) {
-        const bf16x8 ka = *(const bf16x8*)(krow + 16 * ((2 * kk + h) ^ sw));
+      for (int sh = 0; sh < 2; ++sh) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + (32 * sh + n) * C::ROW + 16 * ((2 * kk + h) ^ sw));
         s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], f32x16{}, 0, 0, 0)
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[sh], 0, 0, 0);
       }
@@ -272,20 +271,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 
     // O^T += V^T P^T over the four 16-key chunks
     const unsigned char* Vs = vbuf(j & 1);
+    // (per 16-key chunk: the four d tiles' high-part products, then their low-part products,
+    // so consecutive matrix instructions accumulate into different tiles)
+    const int sub = 8 * (i16 & 1);
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int chunk = 4 * dt + 2 * (G & 1) + ((i16 & 3) >> 1);
-      const int sub = 8 * (i16 & 1);
+    for (int qc = 0; qc < 4; ++qc) {
+      const int r0 = 16 * qc + 4 * h + (i16 >> 2);
+      const int r1 = r0 + 8;
+      bf16x8 va[C::DT];
 #pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        const int r0 = 16 * qc + 4 * h + (i16 >> 2);
-        const int r1 = r0 + 8;
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int chunk = 4 * dt + 2 * (G & 1) + ((i16 & 3) >> 1);
         const bf16x4 v0 = tr_read(Vs + r0 * C::ROW + 16 * (chunk ^ swz(r0)) + sub);
         const bf16x4 v1 = tr_read(Vs + r1 * C::ROW + 16 * (chunk ^ swz(r1)) + sub);
-        const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0, 0, 0);
+        va[dt] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       }
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0, 0, 0);
     }
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
