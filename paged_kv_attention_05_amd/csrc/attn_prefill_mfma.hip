@@ -27,14 +27,16 @@
 //                                             bit-permuted (bits 2 and 3 swapped in each
 //                                             16-key chunk); V^T comes from LDS with the same
 //                                             permutation through two ds_read_tr16_b64.
-// The loop is software-pipelined: the QK^T products of tile j+1 are issued before the softmax
-// of tile j, so the matrix cores and the vector ALUs work at the same time.
+// Two groups of four waves run in ping-pong (one wave of each per SIMD), so one wave's
+// exponentials overlap the other's matrix products (see the loop below).
 // Softmax per row in base 2: one FMA and one v_exp_f32 per score; the running max is only
 // moved (and O rescaled) when a row's max grows by more than 8 (a factor 256), so rescaling
 // is rare; the sum uses the same reference, so the result is exact either way.
 // P is carried as a bf16 pair (truncated high part plus the bf16 rounding of the exact
-// remainder), two products per chunk: ~16 significant bits, where a single bf16 P loses up
-// to 2^-9 of a weight, which against ~10x outlier values exceeds 2e-2.
+// remainder), two products per chunk: ~16 significant bits.  A single bf16 P perturbs each
+// weight by up to 2^-9, which against ~10x outlier values uses most of the 2e-2 budget.
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -63,14 +65,39 @@ struct PrefillCfg {
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-__device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
+// LDS reads at a byte address
+__device__ __forceinline__ bf16x4 tr_read(uint32_t addr) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
   return __builtin_bit_cast(bf16x4, r);
 }
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
 
+// 16 bytes per lane from global memory straight into LDS at lds_wave_base + 16 * lane.  Issued
+// as inline assembly on purpose: the compiler then does not know that the load writes LDS and
+// does not wait for it before every later LDS read (it cannot tell the ring slots apart); the
+// kernel waits for these loads itself (vmcnt before the barrier that publishes them).
+// M0 holds the LDS base of the load.  The compiler treats M0 as reserved and does not accept
+// it as a clobber; nothing else in this file uses M0 (no LDS-DMA builtins, no M0-indexed
+// moves), so setting it here disturbs no compiler-held value.
+__device__ __forceinline__ uint32_t lds_addr(unsigned char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)p;
+}
+// per-lane 64-bit address
 __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds_wave_base)), "v"(g)
+               : "memory");
+}
+// wave-uniform base plus a per-lane 32-bit byte offset
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, unsigned char* lds_wave_base) {
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  // (readfirstlane returns int: go through uint32_t so the low word is not sign-extended)
+  const uint64_t sbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr(lds_wave_base)), "v"(voff),
+               "s"(sbase)
+               : "memory");
 }
 
 template <int D, int WAVES>
@@ -79,9 +106,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   using C = PrefillCfg<D>;
   constexpr int ROWS = 32 * WAVES;
   constexpr int NT = 64 * WAVES;
-  // two K tiles and two V tiles; the output staging reuses the same bytes
+  // three K tiles and three V tiles (a ring); the output staging reuses the same bytes
+  constexpr int NBUF = 3;
   constexpr int OUT_BYTES = ROWS * C::ROW;
-  constexpr int SMEM = (4 * C::TILE) > OUT_BYTES ? (4 * C::TILE) : OUT_BYTES;
+  constexpr int SMEM = (2 * NBUF * C::TILE) > OUT_BYTES ? (2 * NBUF * C::TILE) : OUT_BYTES;
   __shared__ __align__(1024) unsigned char smem[SMEM];
 
   // workgroup -> (item, KV head): consecutive items of one head on one XCD (workgroups are
@@ -139,7 +167,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int32_t ntiles = (kend + kBK - 1) / kBK;
   const int rowoff = (4 * w + (lane >> 4)) & 15;
   const int chunk_sw = (lane & 15) ^ swz(rowoff);
-  const int64_t lane_off = (int64_t)rowoff * row_elems + 8 * chunk_sw;
+  const uint32_t lane_off_b = (uint32_t)(((int64_t)rowoff * row_elems + 8 * chunk_sw) * 2);   // bytes
   const int64_t blk_stride = (int64_t)kBlk * row_elems;
   // Block ids of a full tile (4 consecutive table entries, wave-uniform) are fetched one
   // iteration before they are needed, so no load waits on a table lookup; only the last,
@@ -147,7 +175,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   struct Blocks { int32_t b0, b1, b2, b3; };
   auto fetch_blocks = [&](int32_t j) -> Blocks {
     if (j * kBK + kBK > kend) return Blocks{0, 0, 0, 0};     // partial tile: not used
-    const int32_t* e = table_row + 4 * j;
+    // through the constant address space, so the compiler reads the (wave-uniform) entries
+    // with a scalar load, which does not wait behind the tile loads in flight
+    const __attribute__((address_space(4))) int32_t* e =
+        (const __attribute__((address_space(4))) int32_t*)(table_row + 4 * j);
     return Blocks{e[0], e[1], e[2], e[3]};
   };
   // block of instruction u within the tile: wave-uniform ((w + WAVES*u) / 4)
@@ -159,7 +190,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     if (j * kBK + kBK <= kend) {
 #pragma unroll
       for (int u = 0; u < UK; ++u)
-        load_lds16(base + ((int64_t)pick(bl, u) * blk_stride + lane_off), dst + (w + WAVES * u) * 1024);
+        load_lds16(base + (int64_t)pick(bl, u) * blk_stride, lane_off_b, dst + (w + WAVES * u) * 1024);
     } else {
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
@@ -180,54 +211,158 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 
   // S^T of one K tile (keys 64j .. 64j+63, two halves of 32 keys)
   // (the two halves alternate, so consecutive matrix instructions are independent)
-  auto qk = [&](const unsigned char* Ks, f32x16* s) {
-    const int sw = swz(n);                                  // swz(32 + n) == swz(n)
+  // Per-lane LDS read addresses at ring slot 0, passed through an empty asm so the compiler
+  // keeps them as they are and adds the slot and chunk offsets as read-instruction immediates
+  // (no extra address registers per ring slot).  The V ring sits at LDS offset 0, the K ring
+  // after it.
+  //   K (A operand of QK^T): key row 32*sh + n, chunk (2kk + h) ^ swz(n)   (swz(32+n) == swz(n))
+  //   V (transpose reads):   key rows 16qc + 4h + i16/4 (+8), whose swizzle does not depend on qc
+  uint32_t koff[C::KC], voff[C::DT][2];
+  {
+    const uint32_t kring = lds_addr(smem + NBUF * C::TILE), vring = lds_addr(smem);
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
+      koff[kk] = kring + n * C::ROW + 16 * ((2 * kk + h) ^ swz(n));
+      asm volatile("" : "+v"(koff[kk]));
+    }
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + (32 * sh + n) * C::ROW + 16 * ((2 * kk + h) ^ sw));
-        s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], f32x16{}, 0, 0, 0)
-                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[sh], 0, 0, 0);
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = 4 * h + (i16 >> 2) + 8 * hf;
+        const int chunk = 4 * dt + 2 * (G & 1) + ((i16 & 3) >> 1);
+        voff[dt][hf] = vring + r * C::ROW + 16 * (chunk ^ swz(r)) + 8 * (i16 & 1);
+        asm volatile("" : "+v"(voff[dt][hf]));
       }
+    }
+  }
+  auto qk = [&](int b, f32x16* s) {
+    // K reads in groups of two k-chunks (four reads), each group issued one group ahead of
+    // its products; scheduling fences keep that order
+    auto read_k = [&](int g, bf16x8* ka) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 2 * g + (e >> 1), sh = e & 1;
+        ka[e] = lds_read16(koff[kk] + b * C::TILE + 32 * sh * C::ROW);
+      }
+    };
+    bf16x8 ka[2][4];
+    read_k(0, ka[0]);
+#pragma unroll
+    for (int g = 0; g < C::KC / 2; ++g) {
+      if (g + 1 < C::KC / 2) read_k(g + 1, ka[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 2 * g + (e >> 1), sh = e & 1;
+        s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], f32x16{}, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], s[sh], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Software pipeline: K runs one tile ahead of V.  Iteration j holds K(j+1) and V(j) in LDS,
-  // starts the loads of K(j+2) and V(j+1), computes S(j+1) on the matrix cores while the
-  // vector ALUs turn S(j) into probabilities, then accumulates V(j) P(j).  Buffers: K tile
-  // j in kbuf(j % 2), V tile j in vbuf(j % 2); one barrier per iteration.
-  auto kbuf = [&](int i) { return smem + i * C::TILE; };
-  auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
-  Blocks bl0 = fetch_blocks(0), bl1 = fetch_blocks(1);
-  issue_k(0, bl0, kbuf(0));
-  issue_v(0, bl0, vbuf(0));
-  if (ntiles > 1) issue_k(1, bl1, kbuf(1));
-  Blocks blV = bl1;                                        // blocks of V(j+1)
-  Blocks blK = fetch_blocks(2);                            // blocks of K(j+2)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  f32x16 s_cur[2];
-  qk(kbuf(0), s_cur);
-  __syncthreads();                                          // K(0) read by all before K(2) lands there
 
-  for (int32_t j = 0; j < ntiles; ++j) {
-    if (j + 2 < ntiles) issue_k(j + 2, blK, kbuf(j & 1));
-    if (j + 1 < ntiles) issue_v(j + 1, blV, vbuf((j + 1) & 1));
+
+  // Two wave groups in ping-pong.  Each wave alternates a matrix phase M(i) (O += V(i-1)
+  // P(i-1), then S(i) = QK^T of K tile i) and a vector phase X(i) (mask, running max and the
+  // probabilities P(i) of S(i)).  Waves 0-3 (group A) and 4-7 (group B) hold one wave of each
+  // group per SIMD, and B runs one phase behind A, with a workgroup barrier between phases:
+  // while one wave of a SIMD keeps the matrix core busy, the other does its exponentials.
+  //
+  // Slots (barrier-separated): A runs M(i) in slot 2i and X(i) in slot 2i+1; B runs M(i) in
+  // slot 2i+1 and X(i) in slot 2i+2.  K tile i is read in slots 2i and 2i+1, V tile i in
+  // slots 2i+2 and 2i+3; tile i lives in ring slot i % 3.  At the start of slot 2i every wave
+  // issues its share of K(i+2) and V(i+1) (their ring slots were last read in slot 2i-1);
+  // they have four slots to land: the end of slot 2i+3 waits for them (vmcnt leaves only the
+  // loads issued in slot 2i+2 in flight), before the barrier that opens slot 2i+4.
+  auto vbuf = [&](int b) { return smem + b * C::TILE; };
+  auto kbuf = [&](int b) { return smem + (NBUF + b) * C::TILE; };
+  const bool grp_a = w < WAVES / 2;                          // uniform
+  auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // end of slot 2i+1: the loads issued in slot 2i (2 * UK instructions per tile) may stay in
+  // flight, every earlier one must have landed
+  static_assert(UK == 2, "the wait counts below assume two load instructions per tile and wave");
+  auto bar_loads = [&](int32_t i) {
+    if (i + 2 < ntiles)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (i + 1 < ntiles)
+      asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  {
+    const Blocks bl0 = fetch_blocks(0), bl1 = fetch_blocks(1);
+    issue_k(0, bl0, kbuf(0));
+    issue_v(0, bl0, vbuf(0));
+    if (ntiles > 1) issue_k(1, bl1, kbuf(1));
+  }
+  Blocks blV = fetch_blocks(1);                              // blocks of V(i+1)
+  Blocks blK = fetch_blocks(2);                              // blocks of K(i+2)
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // P = i % 3 is a compile-time constant in every call below (the slot loop is unrolled by
+  // three), so all LDS addresses are per-lane offsets plus immediates
+  auto issue_slot = [&](int32_t i, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (i + 2 < ntiles) issue_k(i + 2, blK, kbuf((P + 2) % NBUF));
+    if (i + 1 < ntiles) issue_v(i + 1, blV, vbuf((P + 1) % NBUF));
     blV = blK;
-    blK = fetch_blocks(j + 3);
-    f32x16 s_next[2];
-    if (j + 1 < ntiles) qk(kbuf((j + 1) & 1), s_next);
+    blK = fetch_blocks(i + 3);
+  };
 
+  f32x16 s[2];
+  u32x4 pb[4], pl[4];
+  // V^T operand of one 16-key chunk for the four d tiles (eight transpose reads)
+  auto read_v = [&](int b, int qc, bf16x8* va) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const bf16x4 v0 = tr_read(voff[dt][0] + b * C::TILE + 16 * qc * C::ROW);
+      const bf16x4 v1 = tr_read(voff[dt][1] + b * C::TILE + 16 * qc * C::ROW);
+      va[dt] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+  };
+  auto phase_m = [&](int32_t i, auto par) {
+    constexpr int P = decltype(par)::value;
+    // PV first: P(i-1) is dead before S(i) is produced, so the two share registers
+    if (i >= 1) {
+      // O^T += V^T P^T over the four 16-key chunks: per chunk the four d tiles' high-part
+      // products, then their low-part products (consecutive matrix instructions accumulate
+      // into different tiles).  The next chunk's V^T reads are issued before this chunk's
+      // products (scheduling fences keep that order), so the matrix core does not wait on LDS.
+      constexpr int Vb = (P + NBUF - 1) % NBUF;
+      bf16x8 va[2][C::DT];
+      read_v(Vb, 0, va[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qc = 0; qc < 4; ++qc) {
+        if (qc < 3) read_v(Vb, qc + 1, va[(qc + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[qc & 1][dt], __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0,
+                                                          0, 0);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[qc & 1][dt], __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0,
+                                                          0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < ntiles) qk(P, s);
+  };
+  auto phase_x = [&](int32_t i) {
+    if (i >= ntiles) return;
     // causal mask on the diagonal tiles only; masked scores are -inf before the max
-    if (j * kBK + kBK - 1 > c + tok0 || Tn < BQ) {
-      const int32_t lim = row_ok ? pos - j * kBK - 4 * h : -1000000;
+    if (i * kBK + kBK - 1 > c + tok0 || Tn < BQ) {
+      const int32_t lim = row_ok ? pos - i * kBK - 4 * h : -1000000;
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * sh + 8 * (r >> 2) + (r & 3);
-          s_cur[sh][r] = off > lim ? kNegInf : s_cur[sh][r];
+          s[sh][r] = off > lim ? kNegInf : s[sh][r];
         }
       }
     }
@@ -235,7 +370,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[sh][r], s_cur[sh][r + 1]));
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[sh][r], s[sh][r + 1]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mxs = mx * sl;                              // mx is finite or -inf, sl > 0
@@ -249,16 +384,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
     }
     const float m_use = m == kNegInf ? 0.f : m;
-
-    u32x4 pb[4], pl[4];
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[sh][8 * kh + jj], sl, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[sh][8 * kh + jj + 1], sl, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj], sl, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj + 1], sl, -m_use));
           lsum += p0 + p1;
           const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
           const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);
@@ -268,41 +401,37 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         }
       }
     }
+  };
 
-    // O^T += V^T P^T over the four 16-key chunks
-    const unsigned char* Vs = vbuf(j & 1);
-    // (per 16-key chunk: the four d tiles' high-part products, then their low-part products,
-    // so consecutive matrix instructions accumulate into different tiles)
-    const int sub = 8 * (i16 & 1);
-#pragma unroll
-    for (int qc = 0; qc < 4; ++qc) {
-      const int r0 = 16 * qc + 4 * h + (i16 >> 2);
-      const int r1 = r0 + 8;
-      bf16x8 va[C::DT];
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int chunk = 4 * dt + 2 * (G & 1) + ((i16 & 3) >> 1);
-        const bf16x4 v0 = tr_read(Vs + r0 * C::ROW + 16 * (chunk ^ swz(r0)) + sub);
-        const bf16x4 v1 = tr_read(Vs + r1 * C::ROW + 16 * (chunk ^ swz(r1)) + sub);
-        va[dt] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0, 0, 0);
-    }
-    s_cur[0] = s_next[0];
-    s_cur[1] = s_next[1];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // K(j+2), V(j+1) have landed
-    __syncthreads();                                        // ... for every thread; tile j consumed
+  // every wave passes 2 * ntiles + 3 barriers in the loop below
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  auto step = [&](int32_t i, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (grp_a) issue_slot(i, par);
+    phase_m(i, par);
+    if (grp_a) bar(); else bar_loads(i);
+    if (!grp_a) issue_slot(i + 1, std::integral_constant<int, (P + 1) % NBUF>{});
+    phase_x(i);
+    if (grp_a) bar_loads(i); else bar();
+  };
+  if (!grp_a) {
+    issue_slot(0, P0{});
+    bar();
   }
+  for (int32_t i = 0; i <= ntiles; i += 3) {
+    step(i, P0{});
+    if (i + 1 <= ntiles) step(i + 1, P1{});
+    if (i + 2 <= ntiles) step(i + 2, P2{});
+  }
+  if (grp_a) bar();
 
   // normalise and stage the tile's output rows in LDS, then write them out coalesced
   lsum += __shfl_xor(lsum, 32);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  __syncthreads();                                          // all waves done with the K/V tiles
+  __syncthreads();                                          // all waves done with the K/V tiles (the
+                                                            // last barrier passed with every load landed)
   __bf16* Os = (__bf16*)smem;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
