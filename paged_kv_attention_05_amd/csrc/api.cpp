@@ -126,6 +126,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.off_small = off; off = align_up(off + sizeof(pa::SmallItem) * (size_t)ns, 256);
   p.off_merge = off; off = align_up(off + sizeof(pa::MergeItem) * (size_t)nm, 256);
   p.off_pf = off;    off = align_up(off + sizeof(pa::PfItem) * (size_t)np, 256);
+  p.off_pf_wide = off; off = align_up(off + sizeof(int32_t) * (size_t)np * Hkv, 256);
   const size_t nparts = nm > 0 ? (size_t)ns * Hkv * pa::kCols : 0;
   p.off_pm = off;    off = align_up(off + 4 * nparts, 256);
   p.off_pl = off;    off = align_up(off + 4 * nparts, 256);

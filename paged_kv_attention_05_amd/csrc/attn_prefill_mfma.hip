@@ -12,17 +12,16 @@
 // of the tensorsofthewall.com post).
 //
 // Data movement: each 64-key K and V tile goes from HBM straight into LDS with the gfx950
-// direct loads (global_load_lds_dwordx4, 16 bytes per lane, no register staging), into
-// double buffers, so the next tiles stream in while the current one is computed (one
-// workgroup barrier per tile).  An LDS row is one key's 256 bytes; its sixteen 16-byte
-// chunks are stored XOR-swizzled (chunk c of row r at slot c ^ f(r), f(r) = 4*(r%4) +
-// (r/4)%4), which makes both the K reads (16 consecutive rows, one chunk) and the V transpose
-// reads (4 rows x 4 chunks) free of bank conflicts.
+// direct loads (global_load_lds_dwordx4, 16 bytes per lane, no register staging), into rings
+// of three tiles, so later tiles stream in while the current one is computed.  An LDS row is
+// one key's 256 bytes; its sixteen 16-byte chunks are stored XOR-swizzled (chunk c of row r
+// at slot c ^ f(r), f(r) = 4*(r%4) + (r/4)%4), which makes both the K reads (16 consecutive
+// rows, one chunk) and the V transpose reads (4 rows x 4 chunks) free of bank conflicts.
 //
 // Compute: wave w owns tile rows 32w .. 32w+31, one row per lane column.
 //   S^T[key][row] = K[key][:] . Q[row][:]     mfma_f32_32x32x16_bf16, K from LDS (A operand,
 //                                             one 16-byte read per lane), Q^T in registers.
-//   O^T[d][row]  += V^T[d][key] P^T[key][row]  mfma_f32_32x32x16_bf16; P^T is the S^T
+//   O^T[d][row]  += V^T[d][key] P^T[key][row]  mfma_f32_32x32x16_f16; P^T is the S^T
 //                                             accumulator layout with the key index
 //                                             bit-permuted (bits 2 and 3 swapped in each
 //                                             16-key chunk); V^T comes from LDS with the same
@@ -32,9 +31,14 @@
 // Softmax per row in base 2: one FMA and one v_exp_f32 per score; the running max is only
 // moved (and O rescaled) when a row's max grows by more than 8 (a factor 256), so rescaling
 // is rare; the sum uses the same reference, so the result is exact either way.
-// P is carried as a bf16 pair (truncated high part plus the bf16 rounding of the exact
-// remainder), two products per chunk: ~16 significant bits.  A single bf16 P perturbs each
-// weight by up to 2^-9, which against ~10x outlier values uses most of the 2e-2 budget.
+//
+// Precision of PV: each V tile is converted in LDS from bf16 to fp16, which is exact for
+// |v| <= 65504, and P is rounded to nearest fp16 (p <= 256 here), with the row sum taken over
+// the same rounded values.  The output is then an exact convex combination of V rows whose
+// weights are off by at most 2^-12 relative: a single bf16 P (2^-9) would use most of the
+// 2e-2 budget against ~10x outlier values.  An item that meets |v| > 65504 is redone by a
+// second kernel that keeps V in bf16 and carries P as a bf16 pair (truncated high part plus
+// the bf16 rounding of the remainder, two products per chunk, ~16 significant bits).
 #include <type_traits>
 
 #include "pa_internal.h"
@@ -48,6 +52,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBK = 64;          // keys per K/V tile
@@ -100,16 +108,22 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, unsi
                : "memory");
 }
 
-template <int D, int WAVES>
+// F16 = true: the fast kernel.  V tiles are converted to fp16 in LDS and P goes to the matrix
+// cores as fp16; a workgroup that meets a V value outside fp16's range (|v| > 65504) flags
+// its item (wide[lin] = 1) and its output is rewritten by the F16 = false kernel, launched
+// right after on the same stream, which keeps V in bf16 and carries P as a bf16 pair.
+template <int D, int WAVES, bool F16>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnArgs a, const PfItem* __restrict__ items,
-                                                                            int32_t n_items) {
+                                                                            int32_t n_items, int32_t* __restrict__ wide) {
   using C = PrefillCfg<D>;
   constexpr int ROWS = 32 * WAVES;
   constexpr int NT = 64 * WAVES;
-  // three K tiles and three V tiles (a ring); the output staging reuses the same bytes
+  // Rings of three tiles each: V as converted to fp16 (fast kernel only), V as loaded (bf16)
+  // and K.  The output staging reuses the first bytes.
   constexpr int NBUF = 3;
+  constexpr int V16_RING = 0, V_RING = F16 ? NBUF * C::TILE : 0, K_RING = V_RING + NBUF * C::TILE;
   constexpr int OUT_BYTES = ROWS * C::ROW;
-  constexpr int SMEM = (2 * NBUF * C::TILE) > OUT_BYTES ? (2 * NBUF * C::TILE) : OUT_BYTES;
+  constexpr int SMEM = (K_RING + NBUF * C::TILE) > OUT_BYTES ? (K_RING + NBUF * C::TILE) : OUT_BYTES;
   __shared__ __align__(1024) unsigned char smem[SMEM];
 
   // workgroup -> (item, KV head): consecutive items of one head on one XCD (workgroups are
@@ -118,6 +132,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int32_t per_xcd = (total + 7) / 8;
   const int32_t lin = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
   if (lin >= total) return;
+  if constexpr (!F16) {
+    if (__builtin_amdgcn_readfirstlane(wide[lin]) == 0) return;   // the fast kernel's output stands
+  }
   const int hkv = lin / n_items;
   const PfItem it = items[lin - hkv * n_items];
 
@@ -213,13 +230,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // (the two halves alternate, so consecutive matrix instructions are independent)
   // Per-lane LDS read addresses at ring slot 0, passed through an empty asm so the compiler
   // keeps them as they are and adds the slot and chunk offsets as read-instruction immediates
-  // (no extra address registers per ring slot).  The V ring sits at LDS offset 0, the K ring
-  // after it.
+  // (no extra address registers per ring slot).
   //   K (A operand of QK^T): key row 32*sh + n, chunk (2kk + h) ^ swz(n)   (swz(32+n) == swz(n))
   //   V (transpose reads):   key rows 16qc + 4h + i16/4 (+8), whose swizzle does not depend on qc
   uint32_t koff[C::KC], voff[C::DT][2];
   {
-    const uint32_t kring = lds_addr(smem + NBUF * C::TILE), vring = lds_addr(smem);
+    const uint32_t kring = lds_addr(smem + K_RING), vring = lds_addr(smem + (F16 ? V16_RING : V_RING));
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
       koff[kk] = kring + n * C::ROW + 16 * ((2 * kk + h) ^ swz(n));
@@ -271,22 +287,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // while one wave of a SIMD keeps the matrix core busy, the other does its exponentials.
   //
   // Slots (barrier-separated): A runs M(i) in slot 2i and X(i) in slot 2i+1; B runs M(i) in
-  // slot 2i+1 and X(i) in slot 2i+2.  K tile i is read in slots 2i and 2i+1, V tile i in
-  // slots 2i+2 and 2i+3; tile i lives in ring slot i % 3.  At the start of slot 2i every wave
-  // issues its share of K(i+2) and V(i+1) (their ring slots were last read in slot 2i-1);
-  // they have four slots to land: the end of slot 2i+3 waits for them (vmcnt leaves only the
-  // loads issued in slot 2i+2 in flight), before the barrier that opens slot 2i+4.
-  auto vbuf = [&](int b) { return smem + b * C::TILE; };
-  auto kbuf = [&](int b) { return smem + (NBUF + b) * C::TILE; };
+  // slot 2i+1 and X(i) in slot 2i+2.  Tile i lives in ring slot i % 3.  K tile i is read in
+  // slots 2i and 2i+1.  V tile i is converted to fp16 in slot 2i (by every wave) and read in
+  // slots 2i+2 and 2i+3.  At the start of slot 2i every wave issues its share of V(i+1), then
+  // of K(i+2) (their ring slots were last read in slot 2i-1).  The end of slot 2i+1 waits
+  // until only the K(i+2) loads may still be in flight (vmcnt counts in issue order): V(i+1)
+  // is converted in slot 2i+2, K(i+2) gets four slots before slot 2i+4 reads it.
+  auto vbuf = [&](int b) { return smem + V_RING + b * C::TILE; };
+  auto kbuf = [&](int b) { return smem + K_RING + b * C::TILE; };
   const bool grp_a = w < WAVES / 2;                          // uniform
   auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  // end of slot 2i+1: the loads issued in slot 2i (2 * UK instructions per tile) may stay in
-  // flight, every earlier one must have landed
   static_assert(UK == 2, "the wait counts below assume two load instructions per tile and wave");
   auto bar_loads = [&](int32_t i) {
     if (i + 2 < ntiles)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (i + 1 < ntiles)
       asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -305,50 +318,87 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // three), so all LDS addresses are per-lane offsets plus immediates
   auto issue_slot = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
-    if (i + 2 < ntiles) issue_k(i + 2, blK, kbuf((P + 2) % NBUF));
     if (i + 1 < ntiles) issue_v(i + 1, blV, vbuf((P + 1) % NBUF));
+    if (i + 2 < ntiles) issue_k(i + 2, blK, kbuf((P + 2) % NBUF));
     blV = blK;
     blK = fetch_blocks(i + 3);
   };
 
+  // V tile i to fp16 (ring slot P), two 16-byte chunks per thread.  bf16 values convert to
+  // fp16 exactly when |v| <= 65504 (fp16's largest finite value; values below 2^-14 become
+  // fp16 subnormals, off by at most 2^-25).  A value out of that range (or an infinity) marks
+  // the item for the bf16 kernel.
+  bool wide_seen = false;                                    // wave-uniform
+  auto convert_v = [&](int32_t i, auto par) {
+    constexpr int P = decltype(par)::value;
+    if constexpr (F16) {
+      if (i >= ntiles) return;
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t off = (uint32_t)(P * C::TILE + 16 * (tid + NT * e));
+        const u32x4 src = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_addr(smem + V_RING) + off);
+        u32x4 dst;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(src[k] << 16), hi = __uint_as_float(src[k] & 0xffff0000u);
+          amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+          const f16x2 hv = {(_Float16)lo, (_Float16)hi};
+          dst[k] = __builtin_bit_cast(uint32_t, hv);
+        }
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_addr(smem + V16_RING) + off) = dst;
+      }
+      wide_seen |= __builtin_amdgcn_ballot_w64(amax > 65504.f) != 0;
+    }
+  };
+
   f32x16 s[2];
-  u32x4 pb[4], pl[4];
+  // P of the last vector phase: fp16 pairs (fast kernel), or the bf16 high parts with pl
+  // holding the bf16 roundings of the remainders
+  u32x4 pb[4], pl[F16 ? 1 : 4];
   // V^T operand of one 16-key chunk for the four d tiles (eight transpose reads)
-  auto read_v = [&](int b, int qc, bf16x8* va) {
+  auto read_v = [&](int b, int qc, u32x4* va) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const bf16x4 v0 = tr_read(voff[dt][0] + b * C::TILE + 16 * qc * C::ROW);
       const bf16x4 v1 = tr_read(voff[dt][1] + b * C::TILE + 16 * qc * C::ROW);
-      va[dt] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      va[dt] = __builtin_bit_cast(u32x4, bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
     }
   };
   auto phase_m = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
     // PV first: P(i-1) is dead before S(i) is produced, so the two share registers
     if (i >= 1) {
-      // O^T += V^T P^T over the four 16-key chunks: per chunk the four d tiles' high-part
-      // products, then their low-part products (consecutive matrix instructions accumulate
-      // into different tiles).  The next chunk's V^T reads are issued before this chunk's
-      // products (scheduling fences keep that order), so the matrix core does not wait on LDS.
+      // O^T += V^T P^T over the four 16-key chunks, per chunk one product per d tile (two in
+      // the bf16 kernel: high parts, then low parts), so consecutive matrix instructions
+      // accumulate into different tiles.  The next chunk's V^T reads are issued before this
+      // chunk's products (scheduling fences keep that order): the matrix core does not wait
+      // on LDS.
       constexpr int Vb = (P + NBUF - 1) % NBUF;
-      bf16x8 va[2][C::DT];
+      u32x4 va[2][C::DT];
       read_v(Vb, 0, va[0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int qc = 0; qc < 4; ++qc) {
         if (qc < 3) read_v(Vb, qc + 1, va[(qc + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F16) {
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[qc & 1][dt], __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0,
-                                                          0, 0);
+          for (int dt = 0; dt < C::DT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[qc & 1][dt]),
+                                                           __builtin_bit_cast(f16x8, pb[qc]), o[dt], 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[qc & 1][dt], __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0,
-                                                          0, 0);
+          for (int dt = 0; dt < C::DT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[qc & 1][dt]),
+                                                            __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0, 0, 0);
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[qc & 1][dt]),
+                                                            __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     if (i < ntiles) qk(P, s);
   };
@@ -392,12 +442,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         for (int jj = 0; jj < 8; jj += 2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj], sl, -m_use));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj + 1], sl, -m_use));
-          lsum += p0 + p1;
-          const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
-          const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);
-          pb[2 * sh + kh][jj >> 1] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);   // {h0.hi16, h1.hi16}
-          const bf16x2 lo = {(__bf16)r0, (__bf16)r1};
-          pl[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, lo);
+          if constexpr (F16) {
+            // rounded to nearest fp16 (p <= 2^kLazy, inside its range); l adds up the same
+            // rounded values, so the output is an exact convex combination of V rows whose
+            // weights are off by at most 2^-12 (relative)
+            const f16x2 pr = {(_Float16)p0, (_Float16)p1};
+            lsum += (float)pr[0] + (float)pr[1];
+            pb[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, pr);
+          } else {
+            lsum += p0 + p1;
+            const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
+            const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);
+            pb[2 * sh + kh][jj >> 1] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);   // {h0.hi16, h1.hi16}
+            const bf16x2 lo = {(__bf16)r0, (__bf16)r1};
+            pl[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, lo);
+          }
         }
       }
     }
@@ -409,15 +468,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   using P2 = std::integral_constant<int, 2>;
   auto step = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
-    if (grp_a) issue_slot(i, par);
+    using Pn = std::integral_constant<int, (P + 1) % NBUF>;
+    if (grp_a) {
+      issue_slot(i, par);
+      convert_v(i, par);
+    }
     phase_m(i, par);
     if (grp_a) bar(); else bar_loads(i);
-    if (!grp_a) issue_slot(i + 1, std::integral_constant<int, (P + 1) % NBUF>{});
+    if (!grp_a) {
+      issue_slot(i + 1, Pn{});
+      convert_v(i + 1, Pn{});
+    }
     phase_x(i);
     if (grp_a) bar_loads(i); else bar();
   };
   if (!grp_a) {
     issue_slot(0, P0{});
+    convert_v(0, P0{});
     bar();
   }
   for (int32_t i = 0; i <= ntiles; i += 3) {
@@ -426,6 +493,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     if (i + 2 <= ntiles) step(i + 2, P2{});
   }
   if (grp_a) bar();
+  if constexpr (F16) {
+    if (wide_seen && lane == 0) wide[lin] = 1;              // redo this item in bf16
+  }
 
   // normalise and stage the tile's output rows in LDS, then write them out coalesced
   lsum += __shfl_xor(lsum, 32);
@@ -468,11 +538,18 @@ int32_t prefill_tile_tokens(int32_t g) { return 32 * kWaves / g; }
 
 hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s) {
   if (p.n_pf == 0) return hipSuccess;
+  if (p.D != 128) return hipErrorInvalidValue;
   const PfItem* items = (const PfItem*)((char*)ws + p.off_pf);
+  int32_t* wide = (int32_t*)((char*)ws + p.off_pf_wide);     // zeroed by the plan kernel
   const int64_t total = p.n_pf * p.Hkv;
   const dim3 grid((unsigned)((total + 7) / 8 * 8));
-  if (p.D != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves>), grid, dim3(64 * kWaves), 0, s, a, items, (int32_t)p.n_pf);
+  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true>), grid, dim3(64 * kWaves), 0, s, a, items, (int32_t)p.n_pf,
+                     wide);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // items whose V left fp16's range (normally none: these workgroups exit at once)
+  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false>), grid, dim3(64 * kWaves), 0, s, a, items,
+                     (int32_t)p.n_pf, wide);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ struct Plan {
   int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed)
   // workspace layout (byte offsets)
-  size_t off_req, off_small, off_merge, off_pf, off_pm, off_pl, off_pacc, total_bytes;
+  size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, total_bytes;
 };
 
 struct alignas(16) SmallItem {

@@ -45,12 +45,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
                                                             ReqOffsets* __restrict__ req,
                                                             SmallItem* __restrict__ small,
                                                             MergeItem* __restrict__ merge,
-                                                            PfItem* __restrict__ pf) {
+                                                            PfItem* __restrict__ pf,
+                                                            int32_t* __restrict__ pf_wide) {
   __shared__ int32_t scan[kPlanThreads];
   __shared__ int32_t o_small[kPlanThreads], o_merge[kPlanThreads], o_pf[kPlanThreads];
   __shared__ int32_t c_t[kPlanThreads], c_ns[kPlanThreads];
   __shared__ int32_t carry[3];
   const int tid = threadIdx.x;
+  // the prefill kernel's per-workgroup "redo in bf16" flags start cleared every call
+  for (int64_t i = tid; i < p.n_pf * p.Hkv; i += kPlanThreads) pf_wide[i] = 0;
   if (tid == 0) carry[0] = carry[1] = carry[2] = 0;
   __syncthreads();
 
@@ -133,7 +136,7 @@ hipError_t launch_plan(const Plan& p, const int32_t* qsl, const int32_t* seq_len
   char* w = (char*)ws;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, qsl, seq_lens,
                      (ReqOffsets*)(w + p.off_req), (SmallItem*)(w + p.off_small),
-                     (MergeItem*)(w + p.off_merge), (PfItem*)(w + p.off_pf));
+                     (MergeItem*)(w + p.off_merge), (PfItem*)(w + p.off_pf), (int32_t*)(w + p.off_pf_wide));
   return hipGetLastError();
 }
 

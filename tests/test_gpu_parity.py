@@ -136,6 +136,51 @@ def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     H.check_batch(b, label=name)
 
 
+def _wide_v_batch():
+    """Two prefill chunks; request 0 has V values past fp16's largest finite value (65504) in
+    three context slots and in one of its new tokens."""
+    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=31)
+    r0 = b.requests[0]
+    pool_v = b.v_cache.view(-1, b.num_kv_heads, b.head_dim)
+    for pos, hk, d, val in [(7, 0, 3, 1.0e5), (260, 5, 100, -2.5e5), (431, 7, 64, 7.0e4)]:
+        pool_v[workloads.slot_of(r0.blocks, pos, b.block_size), hk, d] = val
+    b.v[3, 2, 5] = 9.0e4                 # row 3 of request 0 (position 503)
+    return b
+
+
+def test_prefill_v_beyond_fp16_range():
+    """Such a request takes the bf16 prefill kernel; the other one stays on the fp16 kernel."""
+    H.check_batch(_wide_v_batch(), label="prefill_wide_v")
+
+
+def test_prefill_range_flags_cleared_between_calls():
+    """An ordinary batch gives the same bits before and after a wide-V call that used the same
+    workspace: the per-item redo flags start cleared on every call."""
+    import paged_kv_attention_05_amd as pk
+    dev = torch.device("cuda:0")
+    plain = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                                  head_dim=128, seed=32)
+    wide = _wide_v_batch()
+
+    def run(b, ws):
+        kc, vc = b.k_cache.to(dev), b.v_cache.to(dev)
+        pk.paged_kv_write(b.k.to(dev), b.v.to(dev), b.slot_mapping.to(dev), kc, vc)
+        return pk.paged_attention_varlen(b.q.to(dev), kc, vc, b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                         b.block_table.to(dev), b.block_size, b.scale,
+                                         query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host,
+                                         workspace=ws)
+
+    need = max(pk.paged_attention_workspace_bytes(32, 8, 128, 16, x.query_start_loc_host, x.seq_lens_host,
+                                                  torch.bfloat16) for x in (plain, wide))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    before = run(plain, ws).cpu()
+    run(wide, ws)
+    after = run(plain, ws).cpu()
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+
+
 def test_padding_rows_and_zero_length():
     b = workloads.small_batch([(10, 2), (0, 5), (30, 1)], dtype="bf16", num_heads=8, num_kv_heads=2,
                               head_dim=128, pad_to=7, seed=21)
