@@ -145,8 +145,8 @@ def main() -> int:
 
     # algorithmic work, split the way the library routes requests
     g = batch.num_heads // batch.num_kv_heads
-    prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim in (64, 128) \
-        and 128 % g == 0
+    prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim == 128 \
+        and 256 % g == 0
     is_pf = [prefill_capable and r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
     if kern["prefill"][1] == 0:          # the library routed every request to the small tiles
         is_pf = [False] * len(is_pf)
@@ -174,7 +174,7 @@ def main() -> int:
         t = kern_avg["prefill"] * 1e-3
         tf = w_pf["flops"] / t / 1e12
         prefill = {"kernel": "prefill_tile_mfma", "avg_ms": kern_avg["prefill"], "algorithmic_flops": w_pf["flops"],
-                   "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
+                   "algorithmic_bytes": w_pf["bytes"], "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
 
     # dominant kernel: the one taking the most time per step
     dom = max(("prefill", "small", "kv_write"), key=lambda n: kern_avg[n])
