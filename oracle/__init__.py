@@ -54,7 +54,7 @@ def load_library(path: str):
     lib.oracle_paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_double, P, P,
                                            ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_int64, ctypes.c_int32, P]
+                                           ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32]
     lib.oracle_round_to_bf16.restype = ctypes.c_uint16
     lib.oracle_round_to_bf16.argtypes = [ctypes.c_double]
     return lib
@@ -115,13 +115,15 @@ def gather_context(cache: np.ndarray, table_row: np.ndarray, length: int, dtype:
 def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                     query_start_loc: np.ndarray, seq_lens: np.ndarray, block_table: np.ndarray,
                     scale: float, dtype: str, row_mask: Optional[np.ndarray] = None,
-                    want_f64: bool = False):
+                    want_f64: bool = False, window: int = 0):
     """ReferenceBackend.forward over the pool.
 
     q [N, H, D]; caches [NB+1, bs, Hkv, D]; query_start_loc [R+1]; seq_lens [R];
     block_table [R, W].  Returns out [N, H, D] in `dtype` (and the float64 result if
     want_f64).  With row_mask, only the selected flattened rows are computed; the others
     are left at zero (and NaN in the float64 result) so they cannot pass for results.
+    window > 0: a row at position p sees only keys p - window + 1 .. p (the sliding window
+    of ReferenceBackend.forward); 0 sees every key up to p.
     """
     _check_data(q, dtype, "q")
     _check_data(k_cache, dtype, "k_cache")
@@ -138,7 +140,7 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     rc = _lib().oracle_paged_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(qsl), _ptr(lens),
                                        _ptr(table), bs, float(scale), _ptr(out), _ptr(out64),
                                        len(lens), n, h, hkv, d, table.shape[1], num_slots,
-                                       DTYPES[dtype], _ptr(mask))
+                                       DTYPES[dtype], _ptr(mask), int(window))
     if rc == -1:
         raise ValueError("oracle paged_attention: inconsistent batch metadata")
     if rc != 0:

@@ -20,6 +20,9 @@
  *               table (logical order), then for each of its t query rows i (position
  *               seq_len - t + i) and each query head h: scores over keys 0..position, max,
  *               exponentials, sum, weighted sum of V, divide.  Two passes, no tiling.
+ *               With a sliding window of w > 0 tokens, only the last w of those keys take
+ *               part (keys position-w+1 .. position), as ReferenceBackend.forward's
+ *               `allowed = k_pos > q_pos - window` states in "Attention over the pool".
  *               Requests with seq_len == 0 or no query rows leave their rows at zero.
  *
  * dtype codes: 0 = float32, 1 = bfloat16 (stored as the upper 16 bits of a float32).
@@ -125,7 +128,7 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
                            double* out_f64, int32_t num_reqs, int64_t num_tokens,
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_table_stride, int64_t num_slots, int32_t dtype,
-                           const uint8_t* row_mask) {
+                           const uint8_t* row_mask, int32_t window) {
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0) return -1;
     if (query_start_loc[0] != 0 || query_start_loc[num_reqs] != num_tokens) return -1;
     for (int32_t r = 0; r < num_reqs; ++r) {
@@ -177,6 +180,8 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
                 if (row_mask && !row_mask[row]) continue;
                 const int32_t kvh = h / group;
                 const int32_t q_pos = length - t + i;       /* the last t positions of the context */
+                /* first visible key: 0, or with a window of w tokens the first with k_pos > q_pos - w */
+                const int32_t j0 = (window > 0 && q_pos - window + 1 > 0) ? q_pos - window + 1 : 0;
                 double* s = (double*)malloc(sizeof(double) * (size_t)(q_pos + 1));
                 double* acc = (double*)calloc((size_t)head_dim, sizeof(double));
                 double* qv = (double*)malloc(sizeof(double) * (size_t)head_dim);
@@ -187,9 +192,9 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
                     continue;
                 }
                 for (int32_t d = 0; d < head_dim; ++d) qv[d] = load_elem(q, row * qrow + (int64_t)h * head_dim + d, dtype);
-                /* pass 1: scores of keys 0 .. q_pos and their maximum */
+                /* pass 1: scores of keys j0 .. q_pos and their maximum */
                 double m = -INFINITY;
-                for (int32_t j = 0; j <= q_pos; ++j) {
+                for (int32_t j = j0; j <= q_pos; ++j) {
                     const double* kj = ctx_k + (int64_t)j * kvrow + (int64_t)kvh * head_dim;
                     double dot = 0.0;
                     for (int32_t d = 0; d < head_dim; ++d) dot += qv[d] * kj[d];
@@ -198,7 +203,7 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
                 }
                 /* pass 2: exponentials, their sum and the weighted sum of V */
                 double l = 0.0;
-                for (int32_t j = 0; j <= q_pos; ++j) {
+                for (int32_t j = j0; j <= q_pos; ++j) {
                     const double w = exp(s[j] - m);
                     const double* vj = ctx_v + (int64_t)j * kvrow + (int64_t)kvh * head_dim;
                     l += w;

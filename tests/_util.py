@@ -32,11 +32,13 @@ def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return a.astype(np.float64)
 
 
-def dense_fold_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, computed: int) -> np.ndarray:
+def dense_fold_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, computed: int,
+                         window: int = 0) -> np.ndarray:
     """Causal attention of t query rows at positions computed .. computed + t - 1 over
     contiguous keys 0 .. L-1, written with the grouped-query fold the vllm-lite README prints
     (query heads folded into the row dimension of their KV head, no repeated K), a full
-    score matrix and an explicit bottom-right mask.  q [t,H,D], k/v [L,Hkv,D], float64."""
+    score matrix and an explicit bottom-right mask; window > 0 also masks keys at or before
+    position - window (a band).  q [t,H,D], k/v [L,Hkv,D], float64."""
     t, H, D = q.shape
     L, Hkv, _ = k.shape
     rep = H // Hkv
@@ -44,6 +46,8 @@ def dense_fold_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
     scores = scale * (qg @ k.transpose(1, 2, 0))                 # [Hkv, rep*t, L]
     row_pos = computed + (np.arange(rep * t) % t)                 # query row of each folded row
     allowed = np.arange(L)[None, :] <= row_pos[:, None]
+    if window > 0:
+        allowed &= np.arange(L)[None, :] > row_pos[:, None] - window
     scores = np.where(allowed[None], scores, -np.inf)
     scores = scores - scores.max(axis=2, keepdims=True)
     p = np.exp(scores)
@@ -52,16 +56,20 @@ def dense_fold_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
     return og.reshape(H, t, D).transpose(1, 0, 2)
 
 
-def sdpa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, computed: int) -> np.ndarray:
+def sdpa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, computed: int,
+                   window: int = 0) -> np.ndarray:
     """The same attention through torch's scaled_dot_product_attention in float64 on the
-    CPU, with an explicit bottom-right boolean mask (is_causal aligns top-left) and torch's
-    own grouped-query expansion."""
+    CPU, with an explicit bottom-right boolean mask (is_causal aligns top-left; with a
+    window, a band) and torch's own grouped-query expansion."""
     t, H, D = q.shape
     L = k.shape[0]
     qt = torch.from_numpy(q).permute(1, 0, 2)[None]
     kt = torch.from_numpy(k).permute(1, 0, 2)[None]
     vt = torch.from_numpy(v).permute(1, 0, 2)[None]
-    mask = torch.arange(L)[None, :] <= (computed + torch.arange(t))[:, None]
+    pos = (computed + torch.arange(t))[:, None]
+    mask = torch.arange(L)[None, :] <= pos
+    if window > 0:
+        mask &= torch.arange(L)[None, :] > pos - window
     y = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
                                                          enable_gqa=True)
     return y[0].permute(1, 0, 2).numpy()

@@ -95,18 +95,19 @@ class Scenario:
             table[r, :len(tb)] = tb
         return np.array(qsl, np.int32), np.array(lens, np.int32), table
 
-    def run_oracle(self, orc, scale=None, want_f64=True):
+    def run_oracle(self, orc, scale=None, want_f64=True, window=0):
         qsl, lens, table = self.meta()
         q = np.concatenate(self.q, axis=0) if self.q else np.zeros((0, self.H, self.D), np.float32)
         scale = 1.0 / math.sqrt(self.D) if scale is None else scale
+        kw = {"window": window} if window else {}
         return orc.paged_attention(np.ascontiguousarray(q), self.k_pool, self.v_pool, qsl, lens, table,
-                                   scale, self.dtype, want_f64=want_f64)
+                                   scale, self.dtype, want_f64=want_f64, **kw)
 
-    def dense(self, r, scale=None, ref=dense_fold_attention):
+    def dense(self, r, scale=None, ref=dense_fold_attention, window=0):
         c, t = self.specs[r]
         scale = 1.0 / math.sqrt(self.D) if scale is None else scale
         return ref(as_f64(self.q[r], self.dtype), as_f64(self.ctx_k[r], self.dtype),
-                   as_f64(self.ctx_v[r], self.dtype), scale, c)
+                   as_f64(self.ctx_v[r], self.dtype), scale, c, window=window)
 
 
 def _rel_err(a, b):
@@ -322,6 +323,76 @@ def check_large_scores(orc):
         row += t
 
 
+# ------------------------------------------------------------------------------------------
+# sliding window ("Attention over the pool": allowed = k_pos > q_pos - window)
+# ------------------------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    # specs, H, Hkv, D, bs, windows
+    ([(6, 3), (41, 1), (9, 1), (0, 4)], 8, 4, 48, 16, (1, 2, 5, 16, 40)),
+    ([(60, 10), (1, 1), (0, 23)], 8, 2, 8, 4, (3, 7, 64)),
+]
+
+
+def check_window_dense(orc):
+    for i, (specs, H, Hkv, D, bs, windows) in enumerate(WINDOW_CASES):
+        sc = Scenario(specs, H, Hkv, D, bs, seed=200 + i)
+        for w in windows:
+            _, got = sc.run_oracle(orc, window=w)
+            row = 0
+            for r, (c, t) in enumerate(specs):
+                err = _rel_err(got[row:row + t], sc.dense(r, window=w))
+                assert err < 1e-12, (i, w, r, err)
+                row += t
+
+
+def check_window_sdpa_bf16(orc):
+    sc = Scenario([(20, 5), (0, 9), (33, 1)], 8, 2, 48, 16, dtype="bf16", seed=25)
+    _, got = sc.run_oracle(orc, window=6)
+    row = 0
+    for r, (c, t) in enumerate(sc.specs):
+        assert _rel_err(got[row:row + t], sc.dense(r, ref=sdpa_attention, window=6)) < 1e-12
+        row += t
+
+
+def check_window_one_is_own_v(orc):
+    """A window of one token leaves each row only its own key: the output is its own V row."""
+    sc = Scenario([(12, 4), (0, 3)], 8, 2, 16, 4, seed=26)
+    out, _ = sc.run_oracle(orc, window=1)
+    g, row = sc.H // sc.Hkv, 0
+    for r, (c, t) in enumerate(sc.specs):
+        for i in range(t):
+            for h in range(sc.H):
+                assert np.array_equal(out[row + i, h], sc.ctx_v[r][c + i, h // g]), (r, i, h)
+        row += t
+
+
+def check_window_zero_query_gives_window_mean(orc):
+    """q = 0: every visible score is 0, so row i outputs the mean of its last w values."""
+    sc = Scenario([(10, 5), (0, 8), (29, 1)], 4, 2, 8, 4, seed=27, qzero=True)
+    for w in (2, 3, 11):
+        _, got = sc.run_oracle(orc, window=w)
+        row = 0
+        for r, (c, t) in enumerate(sc.specs):
+            v = as_f64(sc.ctx_v[r], "f32")
+            csum = np.concatenate([np.zeros((1,) + v.shape[1:]), np.cumsum(v, axis=0)])
+            for i in range(t):
+                pos = c + i
+                lo = max(0, pos - w + 1)
+                mean = (csum[pos + 1] - csum[lo]) / (pos + 1 - lo)
+                want = np.repeat(mean, sc.H // sc.Hkv, axis=0)
+                assert np.allclose(got[row + i], want, rtol=1e-12, atol=1e-13), (w, r, i)
+            row += t
+
+
+def check_window_covering_context(orc):
+    """A window at least as long as the context changes nothing, bit for bit."""
+    sc = Scenario([(30, 4), (0, 9), (64, 1)], 8, 2, 8, 4, seed=28)
+    ref = sc.run_oracle(orc, want_f64=False)
+    for w in (65, 66, 1000):
+        assert np.array_equal(sc.run_oracle(orc, want_f64=False, window=w), ref), w
+
+
 def check_padding_rows_zero(orc):
     """Padding rows (seq_len 0, one query row, slot -1) produce zeros, not 0/0."""
     b = workloads.small_batch([(5, 2), (0, 3)], pad_to=5, seed=9)
@@ -456,5 +527,6 @@ ALL_CHECKS = [
     check_bf16_rounding, check_dense_fold, check_dense_sdpa_bf16, check_position_zero_is_v0,
     check_zero_query_gives_prefix_mean, check_constant_values, check_dominant_key, check_large_scores,
     check_padding_rows_zero, check_block_relabelling, check_aliasing, check_batch_composition,
-    check_block_size_invariance, check_rejects_bad_metadata,
+    check_block_size_invariance, check_rejects_bad_metadata, check_window_dense, check_window_sdpa_bf16,
+    check_window_one_is_own_v, check_window_zero_query_gives_window_mean, check_window_covering_context,
 ]

@@ -28,6 +28,9 @@ MUTANTS = [
     ("bf16_via_float", "double r = ldexp(rint(ldexp(x, -q)), q);", "double r = ldexp(rint(ldexp((double)(float)x, -q)), q);"),
     ("padding_rows_not_cleared", "store_elem(out, i * qrow + e, dtype, 0.0);", "store_elem(out, i * qrow + e, dtype, 1.0);"),
     ("head_offset_in_q", "row * qrow + (int64_t)h * head_dim + d, dtype);", "row * qrow + (int64_t)(h / 2) * head_dim + d, dtype);"),
+    ("window_one_key_too_many", "? q_pos - window + 1 : 0;", "? q_pos - window : 0;"),
+    ("window_ignored", "? q_pos - window + 1 : 0;", "? 0 : 0;"),
+    ("window_one_key_too_few", "? q_pos - window + 1 : 0;", "? q_pos - window + 2 : 0;"),
 ]
 
 
