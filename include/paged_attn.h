@@ -96,14 +96,17 @@ size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int
  * where K_j / V_j is position j of the request read from slot
  * block_table[r][j / block_size] * block_size + j % block_size, head kv = h / (H / Hkv)
  * (query heads grouped contiguously onto KV heads).  Requests with seq_len 0 or no rows
- * (padding) produce zero rows.  Arithmetic is float32 (bfloat16 inputs feed bf16 matrix
- * cores with float32 accumulation; probabilities are rounded to bf16 for the PV product);
+ * (padding) produce zero rows.  Arithmetic is float32: bfloat16 inputs feed the matrix
+ * cores with float32 accumulation.  In the PV product, probabilities carry at least 11
+ * significant bits: fp16 probabilities against V converted exactly to fp16 (prefill chunks,
+ * while |v| <= 65504), else a bf16 pair (high part and the bf16 rounding of the remainder).
  * out is rounded to nearest-even.
  *
  * Supported: head_dim in {8, 16, 32, 48, 64, 96, 128, 256}; block_size >= 1 (the bf16
- * matrix-core paths need block_size 16 and head_dim 64 or 128; other shapes use the
- * vector path); num_heads % num_kv_heads == 0; q, out, caches and workspace 16-byte
- * aligned.  workspace must hold paged_attention_workspace_bytes().
+ * matrix-core paths need block_size 16, and head_dim 64 or 128 for decode-like tiles, 128
+ * for prefill chunks; other shapes use the vector path); num_heads % num_kv_heads == 0; q,
+ * out, caches and workspace 16-byte aligned.  workspace must hold
+ * paged_attention_workspace_bytes().
  *
  * Preconditions not checked (unless debug checks are on): block ids in range; the K/V
  * of every visible position has been written.
@@ -117,6 +120,40 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
                            const int32_t* seq_lens_host, int32_t max_query_len,
                            int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                            int32_t dtype, hipStream_t stream);
+
+/*
+ * Options of the _ex entry points; a NULL pointer means all defaults (the plain entry
+ * points above).  reserved[] must be zero.
+ *
+ *   sliding_window  0: a row at position p attends keys 0 .. p.  w > 0: only the last w of
+ *                   them, keys max(0, p - w + 1) .. p: the `window` argument of
+ *                   ReferenceBackend.forward ("Attention over the pool": a key is allowed
+ *                   iff k_pos > q_pos - window).  Blocks wholly before every row's window
+ *                   are not read.  Negative values are rejected (PA_ERR_SHAPE).
+ */
+typedef struct pa_attention_options {
+  int32_t sliding_window;
+  int32_t reserved[7];
+} pa_attention_options;
+
+/* paged_attention_workspace_bytes with options (the workspace depends on the window). */
+size_t paged_attention_workspace_bytes_ex(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          const int32_t* query_start_loc_host,
+                                          const int32_t* seq_lens_host, int32_t dtype,
+                                          const pa_attention_options* options);
+
+/* paged_attention_varlen with options; the same contract otherwise.  The workspace must
+ * hold paged_attention_workspace_bytes_ex() for the same options. */
+int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* query_start_loc, const int32_t* seq_lens,
+                              const int32_t* block_table, int32_t block_size, float scale, void* out,
+                              int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                              int64_t num_slots, const int32_t* query_start_loc_host,
+                              const int32_t* seq_lens_host, int32_t max_query_len,
+                              int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                              int32_t dtype, hipStream_t stream, const pa_attention_options* options);
 
 /*
  * paged_attn_set_debug_checks: when enable != 0, later calls on this thread also copy

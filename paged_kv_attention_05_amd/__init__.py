@@ -8,7 +8,8 @@ there is no fallback.
 Names follow the C ABI in ``include/paged_attn.h``:
     paged_kv_write(k, v, slot_mapping, k_cache, v_cache)
     paged_attention_varlen(q, k_cache, v_cache, query_start_loc, seq_lens, block_table,
-                           block_size, scale, out, query_start_loc_host=..., seq_lens_host=...)
+                           block_size, scale, out, query_start_loc_host=..., seq_lens_host=...,
+                           sliding_window=0)     (calls paged_attention_varlen_ex)
 """
 from __future__ import annotations
 
@@ -25,11 +26,17 @@ PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
           -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
 EXPORTS = ["paged_kv_write", "paged_attention_varlen", "paged_attention_workspace_bytes",
+           "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
            "paged_attn_set_timing", "paged_attn_timing_report"]
 KINDS = ["kv_write", "plan", "prefill", "small", "merge"]
 
 _lib = None
+
+
+class AttentionOptions(ctypes.Structure):
+    """pa_attention_options of the C ABI."""
+    _fields_ = [("sliding_window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
 class PagedAttnError(RuntimeError):
@@ -54,6 +61,12 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attention_varlen.restype = ctypes.c_int
     lib.paged_attention_varlen.argtypes = [P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I64, I32, I32,
                                            I32, I32, I64, P, P, I32, I32, P, SZ, I32, P]
+    OPT = ctypes.POINTER(AttentionOptions)
+    lib.paged_attention_workspace_bytes_ex.restype = SZ
+    lib.paged_attention_workspace_bytes_ex.argtypes = [I32, I64, I32, I32, I32, I32, P, P, I32, OPT]
+    lib.paged_attention_varlen_ex.restype = ctypes.c_int
+    lib.paged_attention_varlen_ex.argtypes = [P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I64, I32, I32,
+                                              I32, I32, I64, P, P, I32, I32, P, SZ, I32, P, OPT]
     lib.paged_attn_last_error.restype = ctypes.c_char_p
     lib.paged_attn_last_error.argtypes = []
     lib.paged_attn_set_debug_checks.restype = None
@@ -136,15 +149,22 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                               PA_DTYPE[k.dtype], PA_DTYPE[k_cache.dtype], _stream(stream)))
 
 
+def _options(sliding_window: int):
+    opts = AttentionOptions()
+    opts.sliding_window = int(sliding_window)
+    return ctypes.byref(opts), opts
+
+
 def paged_attention_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                                     query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
-                                    dtype: torch.dtype) -> int:
+                                    dtype: torch.dtype, sliding_window: int = 0) -> int:
     lib = load_library()
     r = len(seq_lens_host)
     n = int(query_start_loc_host[-1]) if r else 0
-    return int(lib.paged_attention_workspace_bytes(r, n, num_heads, num_kv_heads, head_dim, block_size,
-                                                   _host_i32(query_start_loc_host), _host_i32(seq_lens_host),
-                                                   PA_DTYPE[dtype]))
+    ref, _keep = _options(sliding_window)
+    return int(lib.paged_attention_workspace_bytes_ex(r, n, num_heads, num_kv_heads, head_dim, block_size,
+                                                      _host_i32(query_start_loc_host), _host_i32(seq_lens_host),
+                                                      PA_DTYPE[dtype], ref))
 
 
 def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -152,8 +172,10 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            block_size: int, scale: float, out: Optional[torch.Tensor] = None, *,
                            query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
                            max_query_len: int = 0, max_seq_len: int = 0,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Causal attention of the flattened batch over the pool; returns out [N, H, D]."""
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           sliding_window: int = 0) -> torch.Tensor:
+    """Causal attention of the flattened batch over the pool; returns out [N, H, D].
+    sliding_window > 0 limits the row at position p to keys p - sliding_window + 1 .. p."""
     lib = load_library()
     n, h, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[1] != block_size or k_cache.shape[3] != d:
@@ -168,15 +190,16 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     hkv = k_cache.shape[2]
     r = len(seq_lens_host)
     qh, sh = _host_i32(query_start_loc_host), _host_i32(seq_lens_host)
-    need = lib.paged_attention_workspace_bytes(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype])
+    ref, _keep = _options(sliding_window)
+    need = lib.paged_attention_workspace_bytes_ex(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype], ref)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
     stride = block_table.shape[1] if block_table.dim() == 2 else 0
     num_slots = k_cache.shape[0] * k_cache.shape[1]
-    _check(lib.paged_attention_varlen(
+    _check(lib.paged_attention_varlen_ex(
         _dptr(q, "q"), _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"),
         _dptr(query_start_loc, "query_start_loc"), _dptr(seq_lens, "seq_lens"), _dptr(block_table, "block_table"),
         block_size, float(scale), _dptr(out, "out"), r, n, h, hkv, d, stride, num_slots, qh, sh,
         int(max_query_len), int(max_seq_len), _dptr(workspace, "workspace"), workspace.numel(),
-        PA_DTYPE[q.dtype], _stream(stream)))
+        PA_DTYPE[q.dtype], _stream(stream), ref))
     return out

@@ -62,9 +62,20 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Options of the _ex entry points (NULL: defaults).  Reserved fields must be zero.
+int read_options(const pa_attention_options* o, int32_t* window) {
+  *window = 0;
+  if (!o) return PA_OK;
+  for (int32_t x : o->reserved)
+    if (x != 0) return fail(PA_ERR_SHAPE, "pa_attention_options.reserved must be zero");
+  if (o->sliding_window < 0) return fail(PA_ERR_SHAPE, "sliding_window must be >= 0");
+  *window = o->sliding_window;
+  return PA_OK;
+}
+
 // Validates the host metadata and builds the plan.  Returns PA_OK or an error code.
 int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t bs, int32_t stride,
-              const int32_t* qsl, const int32_t* lens, int32_t dtype, pa::Plan* out) {
+              const int32_t* qsl, const int32_t* lens, int32_t dtype, int32_t window, pa::Plan* out) {
   if (R < 0 || N < 0) return fail(PA_ERR_METADATA, "num_reqs and num_tokens must be >= 0");
   if (N > INT32_MAX) return fail(PA_ERR_SHAPE, "num_tokens must fit in int32");
   if (H <= 0 || Hkv <= 0 || H % Hkv != 0)
@@ -80,8 +91,10 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
     if (qsl[0] != 0) return fail(PA_ERR_METADATA, "query_start_loc[0] must be 0");
     if ((int64_t)qsl[R] != N) return fail(PA_ERR_METADATA, "query_start_loc[num_reqs] must equal num_tokens");
   }
+  if (window < 0) return fail(PA_ERR_SHAPE, "sliding_window must be >= 0");
   pa::Plan p{};
   p.R = R; p.H = H; p.Hkv = Hkv; p.g = H / Hkv; p.D = D; p.bs = bs;
+  p.window = window;
   if (p.g >= pa::kCols) { p.tile_heads = pa::kCols; p.tile_tokens = 1; }
   else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
   p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
@@ -102,7 +115,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
     if ((int64_t)(L + bs - 1) / bs > stride)
       return fail(PA_ERR_METADATA, "block_table_stride too small for seq_len of request " + std::to_string(r));
     if (t > 0 && L > 0 && !pa::use_prefill_path(p, t, L))
-      small_keys += (double)L * ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+      small_keys += (double)pa::small_key_span(p, L) * ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
   }
   // Key splits: enough workgroups to fill 256 compute units several times over, but at
   // most 1024 keys per split so long contexts are cut into balanced pieces.
@@ -207,10 +220,21 @@ size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int
                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                        const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
                                        int32_t dtype) {
+  return paged_attention_workspace_bytes_ex(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                                            query_start_loc_host, seq_lens_host, dtype, nullptr);
+}
+
+size_t paged_attention_workspace_bytes_ex(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                          int32_t dtype, const pa_attention_options* options) {
   pa::Plan p;
   const std::string keep = g_last_error;
-  const int rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, INT32_MAX,
-                           query_start_loc_host, seq_lens_host, dtype, &p);
+  int32_t window = 0;
+  int rc = read_options(options, &window);
+  if (rc == PA_OK)
+    rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, INT32_MAX,
+                   query_start_loc_host, seq_lens_host, dtype, window, &p);
   g_last_error = keep;
   return rc == PA_OK ? p.total_bytes : 0;
 }
@@ -224,13 +248,31 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
                            const int32_t* seq_lens_host, int32_t max_query_len,
                            int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                            int32_t dtype, hipStream_t stream) {
+  return paged_attention_varlen_ex(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, block_size, scale,
+                                   out, num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_table_stride,
+                                   num_slots, query_start_loc_host, seq_lens_host, max_query_len, max_seq_len,
+                                   workspace, workspace_bytes, dtype, stream, nullptr);
+}
+
+int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* query_start_loc, const int32_t* seq_lens,
+                              const int32_t* block_table, int32_t block_size, float scale, void* out,
+                              int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                              int64_t num_slots, const int32_t* query_start_loc_host,
+                              const int32_t* seq_lens_host, int32_t max_query_len,
+                              int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                              int32_t dtype, hipStream_t stream, const pa_attention_options* options) {
   g_last_error.clear();
   (void)max_query_len;
   (void)max_seq_len;
   if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
+  int32_t window = 0;
+  int rc = read_options(options, &window);
+  if (rc != PA_OK) return rc;
   pa::Plan p;
-  int rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                     query_start_loc_host, seq_lens_host, dtype, &p);
+  rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                 query_start_loc_host, seq_lens_host, dtype, window, &p);
   if (rc != PA_OK) return rc;
   if (num_reqs == 0) return PA_OK;
   if (!query_start_loc || !seq_lens || !block_table || !workspace) return fail(PA_ERR_NULL, "null pointer argument");
@@ -262,6 +304,7 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
   a.bs = block_size; a.stride = block_table_stride; a.H = num_heads; a.Hkv = num_kv_heads;
   a.g = p.g; a.D = head_dim; a.tile_tokens = p.tile_tokens; a.tile_heads = p.tile_heads;
   a.split_keys = p.split_keys;
+  a.window = p.window;
   a.scale_log2e = scale * 1.4426950408889634f;
 
   hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });

@@ -111,7 +111,8 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   const int ni = n / a.tile_heads, nj = n - ni * a.tile_heads;
   const bool col_ok = ni < Tn && nj < HGn;
   const int32_t pos = c + it.tok0 + ni;
-  const int32_t kb = it.split * a.split_keys;                   // multiple of 64
+  const int32_t lo = a.window > 0 ? pos - a.window : -1;        // keys <= lo are outside the window
+  const int32_t kb = small_key_base(a.window, c + it.tok0) + it.split * a.split_keys;   // multiple of 64
   const int32_t ke = min(c + it.tok0 + Tn, kb + a.split_keys);
   const int32_t* table_row = a.block_table + (int64_t)it.r * a.stride;
   const int64_t row_elems = (int64_t)a.Hkv * D;
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     const int32_t key0 = lb * kBlk + 4 * G;
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (col_ok && key0 + i < ke && key0 + i <= pos) ? s[i] : kNegInf;
+    for (int i = 0; i < 4; ++i)
+      sv[i] = (col_ok && key0 + i < ke && key0 + i <= pos && key0 + i > lo) ? s[i] : kNegInf;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));

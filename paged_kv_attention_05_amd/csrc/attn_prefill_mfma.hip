@@ -181,7 +181,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // for every instruction, so a full tile costs one table lookup per block.  Keys at or past
   // kend (last tile only) read key kend-1 instead: finite data, masked out.
   constexpr int UK = kBK / 4 / WAVES;                         // instructions per wave per tile
-  const int32_t ntiles = (kend + kBK - 1) / kBK;
+  // With a sliding window the tile's first row sees keys from c + tok0 - window + 1 on: the
+  // K/V tiles before the one holding that key are skipped.  Tile i of the loop below is
+  // key tile t0 + i.
+  const int32_t t0 = a.window > 0 ? max(0, c + tok0 - a.window + 1) / kBK : 0;
+  const int32_t ntiles = (kend + kBK - 1) / kBK - t0;
   const int rowoff = (4 * w + (lane >> 4)) & 15;
   const int chunk_sw = (lane & 15) ^ swz(rowoff);
   const uint32_t lane_off_b = (uint32_t)(((int64_t)rowoff * row_elems + 8 * chunk_sw) * 2);   // bytes
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // partial tile computes clamped per-lane keys.
   struct Blocks { int32_t b0, b1, b2, b3; };
   auto fetch_blocks = [&](int32_t j) -> Blocks {
+    j += t0;
     if (j * kBK + kBK > kend) return Blocks{0, 0, 0, 0};     // partial tile: not used
     // through the constant address space, so the compiler reads the (wave-uniform) entries
     // with a scalar load, which does not wait behind the tile loads in flight
@@ -204,6 +209,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     return bi == 0 ? bl.b0 : bi == 1 ? bl.b1 : bi == 2 ? bl.b2 : bl.b3;
   };
   auto issue = [&](const __bf16* base, int32_t j, const Blocks& bl, unsigned char* dst) {
+    j += t0;
     if (j * kBK + kBK <= kend) {
 #pragma unroll
       for (int u = 0; u < UK; ++u)
@@ -404,15 +410,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   };
   auto phase_x = [&](int32_t i) {
     if (i >= ntiles) return;
-    // causal mask on the diagonal tiles only; masked scores are -inf before the max
-    if (i * kBK + kBK - 1 > c + tok0 || Tn < BQ) {
-      const int32_t lim = row_ok ? pos - i * kBK - 4 * h : -1000000;
+    // causal mask on the diagonal tiles, window mask on the tiles holding some row's window
+    // start; masked scores are -inf before the max.  This lane's score r is key kt + off + 4h.
+    const int32_t kt = (i + t0) * kBK;
+    const bool diag = kt + kBK - 1 > c + tok0 || Tn < BQ;
+    const bool edge = a.window > 0 && kt <= c + tok0 + Tn - 1 - a.window;
+    if (diag || edge) {
+      const int32_t lim = row_ok ? pos - kt - 4 * h : -1000000;      // off > lim: after the row
+      // off <= lo: before the row's window (clamped to -1 .. 64 so it cannot overflow)
+      const int64_t lo64 = (a.window > 0 && row_ok) ? (int64_t)pos - a.window - kt - 4 * h : -1;
+      const int32_t lo = (int32_t)(lo64 < -1 ? -1 : (lo64 > 64 ? 64 : lo64));
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * sh + 8 * (r >> 2) + (r & 3);
-          s[sh][r] = off > lim ? kNegInf : s[sh][r];
+          s[sh][r] = (off > lim || off <= lo) ? kNegInf : s[sh][r];
         }
       }
     }

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
   const int ni = n / a.tile_heads, nj = n - ni * a.tile_heads;
   const bool col_ok = ni < Tn && nj < HGn;
   const int32_t pos = c + it.tok0 + ni;                      // this column's position
-  const int32_t kb = it.split * a.split_keys;
+  const int32_t lo = a.window > 0 ? pos - a.window : -1;      // keys <= lo are outside the window
+  const int32_t kb = small_key_base(a.window, c + it.tok0) + it.split * a.split_keys;
   const int32_t ke = min(c + it.tok0 + Tn, kb + a.split_keys);
   const int32_t* table_row = a.block_table + (int64_t)it.r * a.stride;
   const T* kc = (const T*)a.k_cache;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
     for (int i = 0; i < 4; ++i) {
       const int32_t key = k0 + 4 * G + i;
       s[i] = kNegInf;
-      if (key < ke && col_ok && key <= pos) {
+      if (key < ke && col_ok && key <= pos && key > lo) {
         const T* kp = kc + slot_of(table_row, key, a.bs) * row_elems + (int64_t)hkv * D;
         float dot = 0.f;
 #pragma unroll

@@ -43,6 +43,7 @@ struct Plan {
   int32_t split_keys;              // keys per split of a small tile
   int32_t pf_tokens;               // 0: prefill path off
   int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
+  int32_t window;                  // sliding window in tokens (0: none)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed)
   // workspace layout (byte offsets)
   size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, total_bytes;
@@ -68,8 +69,23 @@ struct alignas(16) ReqOffsets {
 __host__ __device__ __forceinline__ bool use_prefill_path(const Plan& p, int32_t t, int32_t L) {
   return p.pf_tokens > 0 && L > 0 && t * p.g > kCols;
 }
+// Keys one small tile of a request with context L can see: all L, or with a sliding window
+// of w tokens at most w + tile_tokens - 1 (the tile's rows are consecutive), plus up to 63
+// because a tile's key range starts at a multiple of 64.
+__host__ __device__ __forceinline__ int32_t small_key_span(const Plan& p, int32_t L) {
+  if (p.window <= 0) return L;
+  const int64_t span = (int64_t)p.window + p.tile_tokens + 62;
+  return span < L ? (int32_t)span : L;
+}
+// First key of a small tile whose first row is at position pos0: 0, or the window start
+// rounded down to a multiple of 64 (the key splits of the tile start there).
+__host__ __device__ __forceinline__ int32_t small_key_base(int32_t window, int32_t pos0) {
+  if (window <= 0 || pos0 - window + 1 <= 0) return 0;
+  return ((pos0 - window + 1) / 64) * 64;
+}
 __host__ __device__ __forceinline__ int32_t small_nsplit(const Plan& p, int32_t L) {
-  return L <= 0 ? 1 : (L + p.split_keys - 1) / p.split_keys;
+  const int32_t span = small_key_span(p, L);
+  return span <= 0 ? 1 : (span + p.split_keys - 1) / p.split_keys;
 }
 __host__ __device__ __forceinline__ void request_counts(const Plan& p, int32_t t, int32_t L,
                                                         int32_t* n_small, int32_t* n_merge,
@@ -99,6 +115,8 @@ struct AttnArgs {
   void* out;
   int32_t bs, stride, H, Hkv, g, D;
   int32_t tile_tokens, tile_heads, split_keys;
+  int32_t window;                    // sliding window in tokens: a row at position p sees keys
+                                     // p - window + 1 .. p; 0: keys 0 .. p
   float scale_log2e;                 // scale * log2(e): scores are kept in base 2
 };
 

@@ -27,7 +27,7 @@ def record(entry: dict) -> None:
             f.write(json.dumps(entry) + "\n")
 
 
-def gpu_step(batch, path: int = 0, write: bool = True, out_dtype=None):
+def gpu_step(batch, path: int = 0, write: bool = True, out_dtype=None, window: int = 0):
     """KV write then attention on cuda:0; returns (out, k_cache, v_cache) on the CPU."""
     dev = torch.device("cuda:0")
     pk.set_path(path)
@@ -40,21 +40,21 @@ def gpu_step(batch, path: int = 0, write: bool = True, out_dtype=None):
                                   batch.block_table.to(dev), batch.block_size, batch.scale, out,
                                   query_start_loc_host=batch.query_start_loc_host,
                                   seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
-                                  max_seq_len=batch.max_seq_len)
+                                  max_seq_len=batch.max_seq_len, sliding_window=window)
         torch.cuda.synchronize()
         return out.cpu(), kc.cpu(), vc.cpu()
     finally:
         pk.set_path(0)
 
 
-def oracle_step(batch, row_mask: Optional[np.ndarray] = None, write: bool = True):
+def oracle_step(batch, row_mask: Optional[np.ndarray] = None, write: bool = True, window: int = 0):
     """The oracle's KV write then attention; returns (float64 out, k_cache, v_cache) as numpy."""
     kc, vc = to_np(batch.k_cache).copy(), to_np(batch.v_cache).copy()
     if write:
         oracle.kv_write(to_np(batch.k), to_np(batch.v), batch.slot_mapping.numpy(), kc, vc, batch.dtype, batch.dtype)
     _, out64 = oracle.paged_attention(to_np(batch.q), kc, vc, batch.query_start_loc.numpy(), batch.seq_lens.numpy(),
                                       batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=row_mask,
-                                      want_f64=True)
+                                      want_f64=True, window=window)
     return out64, kc, vc
 
 
@@ -65,19 +65,21 @@ def assert_pools_equal(gpu_cache: torch.Tensor, oracle_cache: np.ndarray) -> Non
     assert np.array_equal(g[:-1].view(np.uint8), o[:-1].view(np.uint8)), "pool differs from the oracle's"
 
 
-def check_batch(batch, path: int = 0, row_mask: Optional[np.ndarray] = None, label: str = "") -> float:
+def check_batch(batch, path: int = 0, row_mask: Optional[np.ndarray] = None, label: str = "",
+                window: int = 0) -> float:
     """Full parity of one step: pools bit-exact, attention within the bound on every row
     (or the rows of row_mask).  Returns the error as a multiple of the bound."""
-    log(f"[parity] {label or batch.name}: N={batch.num_tokens} R={batch.num_reqs} dtype={batch.dtype} path={path}")
-    out, kc, vc = gpu_step(batch, path=path)
-    ref64, okc, ovc = oracle_step(batch, row_mask=row_mask)
+    log(f"[parity] {label or batch.name}: N={batch.num_tokens} R={batch.num_reqs} dtype={batch.dtype} path={path}"
+        f" window={window}")
+    out, kc, vc = gpu_step(batch, path=path, window=window)
+    ref64, okc, ovc = oracle_step(batch, row_mask=row_mask, window=window)
     assert_pools_equal(kc, okc)
     assert_pools_equal(vc, ovc)
     got = out.float().numpy()
     rows = slice(None) if row_mask is None else np.nonzero(row_mask)[0]
     err = attention_error(got[rows], ref64[rows], batch.dtype)
     log(f"[parity] {label or batch.name}: error {err:.3g} x bound")
-    entry = {"case": label or batch.name, "dtype": batch.dtype, "path": path, "error_x_bound": err,
+    entry = {"case": label or batch.name, "dtype": batch.dtype, "path": path, "window": window, "error_x_bound": err,
              "rows_checked": int(len(got) if row_mask is None else row_mask.sum())}
     if batch.dtype == "bf16":
         entry["excess_over_rounding_x_2e-2"] = rounding_excess(got[rows], ref64[rows])

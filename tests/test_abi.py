@@ -82,3 +82,35 @@ def test_kv_write_rejects_bad_arguments():
 def test_binding_requires_the_library(tmp_path):
     with pytest.raises(RuntimeError):
         pk.load_library(str(tmp_path / "missing.so"))
+
+
+def _call_ex(opts, lens=(5,), qsl=(0, 1)):
+    lib = pk.load_library()
+    return lib.paged_attention_varlen_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1, FAKE, len(lens), qsl[-1], 8, 2,
+                                         128, 4, 1024, _host(list(qsl)), _host(list(lens)), 0, 0, FAKE, 16, 1, None,
+                                         ctypes.byref(opts) if opts is not None else None)
+
+
+def test_options_are_validated():
+    bad = pk.AttentionOptions()
+    bad.sliding_window = -3
+    assert _call_ex(bad) == -2 and "sliding_window" in pk.load_library().paged_attn_last_error().decode()
+    bad = pk.AttentionOptions()
+    bad.reserved[2] = 1
+    assert _call_ex(bad) == -2 and "reserved" in pk.load_library().paged_attn_last_error().decode()
+    # valid options (or none) get as far as the workspace check
+    assert _call_ex(pk.AttentionOptions()) == -5
+    assert _call_ex(None) == -5
+
+
+def test_window_shrinks_the_split_workspace():
+    """Long decodes split their keys over workgroups; a short window needs fewer splits."""
+    lib = pk.load_library()
+    qsl, lens = _host([0, 1, 2]), _host([30000, 20000])
+    full = lib.paged_attention_workspace_bytes(2, 2, 8, 2, 128, 16, qsl, lens, 1)
+    opts = pk.AttentionOptions()
+    opts.sliding_window = 256
+    windowed = lib.paged_attention_workspace_bytes_ex(2, 2, 8, 2, 128, 16, qsl, lens, 1, ctypes.byref(opts))
+    assert 0 < windowed < full
+    opts.sliding_window = 0
+    assert lib.paged_attention_workspace_bytes_ex(2, 2, 8, 2, 128, 16, qsl, lens, 1, ctypes.byref(opts)) == full

@@ -136,6 +136,39 @@ def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     H.check_batch(b, label=name)
 
 
+# ------------------------------------------------------------------------- sliding window
+WINDOW = [
+    # (name, specs (computed, new), H, Hkv, D, bs, dtype, windows)
+    ("decodes_bf16", [(1000, 1), (15, 1), (300, 1), (5000, 1), (0, 1)], 32, 8, 128, 16, "bf16", (1, 16, 100, 4096)),
+    ("prefill_bf16", [(700, 150), (90, 1), (0, 300)], 32, 8, 128, 16, "bf16", (1, 63, 64, 65, 200, 1000)),
+    ("spec_rows_bf16", [(100, 2), (57, 3), (300, 4), (16, 5)], 8, 2, 128, 16, "bf16", (2, 7)),
+    ("vector_f32", [(60, 10), (1, 1), (0, 23), (3000, 1)], 8, 2, 48, 4, "f32", (1, 5, 64, 1000)),
+    ("decodes_d64_long", [(20000, 1), (9000, 1)], 8, 1, 64, 16, "bf16", (300, 5000)),
+]
+
+
+@pytest.mark.parametrize("name,specs,h,hkv,d,bs,dtype,windows", WINDOW, ids=[w[0] for w in WINDOW])
+def test_sliding_window(name, specs, h, hkv, d, bs, dtype, windows):
+    b = workloads.small_batch(specs, dtype=dtype, num_heads=h, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                              seed=zlib.crc32(name.encode()) % 1000)
+    for w in windows:
+        H.check_batch(b, label=f"window_{name}_{w}", window=w)
+
+
+def test_window_covering_every_context_changes_nothing():
+    b = workloads.small_batch([(700, 150), (90, 1), (3000, 1)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=41)
+    ref, _, _ = H.gpu_step(b)
+    for w in (3001, 1 << 30):
+        got, _, _ = H.gpu_step(b, window=w)
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), w
+
+
+def test_long_context_full_size_window():
+    b = workloads.long_context()
+    H.check_batch(b, row_mask=_sample_rows(b, 6), label="long_context_window_4096", window=4096)
+
+
 def _wide_v_batch():
     """Two prefill chunks; request 0 has V values past fp16's largest finite value (65504) in
     three context slots and in one of its new tokens."""
