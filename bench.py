@@ -69,6 +69,8 @@ def main() -> int:
     ap.add_argument("--cpu-prefill-rows", type=int, default=256,
                     help="prefill rows in the oracle's timed sample (plus every decode row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (0: none); the workload is otherwise unchanged")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once: a plain copy "
                          "of known size whose HBM counters scale the kernels' counters")
@@ -105,7 +107,7 @@ def main() -> int:
     out = torch.empty_like(q)
     ws_bytes = pk.paged_attention_workspace_bytes(batch.num_heads, batch.num_kv_heads, batch.head_dim,
                                                   batch.block_size, batch.query_start_loc_host,
-                                                  batch.seq_lens_host, q.dtype)
+                                                  batch.seq_lens_host, q.dtype, sliding_window=args.window)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def step():
@@ -113,7 +115,7 @@ def main() -> int:
         pk.paged_attention_varlen(q, kc, vc, qsl, lens, table, batch.block_size, batch.scale, out,
                                   query_start_loc_host=batch.query_start_loc_host,
                                   seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
-                                  max_seq_len=batch.max_seq_len, workspace=ws)
+                                  max_seq_len=batch.max_seq_len, workspace=ws, sliding_window=args.window)
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -152,9 +154,9 @@ def main() -> int:
         is_pf = [False] * len(is_pf)
     pf_ids = [i for i, f in enumerate(is_pf) if f]
     dec_ids = [i for i, f in enumerate(is_pf) if not f]
-    w_all = attention_work(batch)
-    w_dec = attention_work(batch, dec_ids) if dec_ids else None
-    w_pf = attention_work(batch, pf_ids) if pf_ids else None
+    w_all = attention_work(batch, window=args.window)
+    w_dec = attention_work(batch, dec_ids, window=args.window) if dec_ids else None
+    w_pf = attention_work(batch, pf_ids, window=args.window) if pf_ids else None
     w_write = write_work(batch)
     peak_flops = PEAK_BF16_TFLOPS if batch.dtype == "bf16" else PEAK_F32_TFLOPS
     t_star = max((w_all["bytes"] + w_write["bytes"]) / (PEAK_HBM_GBPS * 1e9), w_all["flops"] / (peak_flops * 1e12))
@@ -191,7 +193,7 @@ def main() -> int:
         roof = {"kernel": "kv_copy16", "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gb / PEAK_HBM_GBPS, "algorithmic_per_launch": w_write["bytes"],
                 "avg_launch_ms": kern_avg["kv_write"]}
-    roof["traffic"] = measured_traffic(dom, args.workload)
+    roof["traffic"] = measured_traffic(dom, args.workload + (f"_window{args.window}" if args.window else ""))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -199,7 +201,7 @@ def main() -> int:
         # grouped heads fit 16 columns (decodes), and a spread of rows from the longer chunks
         chunk = [r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
         cpu = cpu_baseline(batch, args.cpu_prefill_rows, [i for i, f in enumerate(chunk) if not f],
-                           [i for i, f in enumerate(chunk) if f], peak_flops)
+                           [i for i, f in enumerate(chunk) if f], peak_flops, args.window)
 
     line = {
         "metric": METRIC, "value": value, "unit": "% of MI355X peak", "n_gpus": 1, "steps": args.steps,
@@ -208,7 +210,7 @@ def main() -> int:
         "config": {"workload": batch.name, "description": batch.description, "num_tokens": batch.num_tokens,
                    "num_reqs": batch.num_reqs, "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
                    "head_dim": batch.head_dim, "block_size": batch.block_size, "pool_blocks": batch.num_blocks,
-                   "parallelism": "single-gpu"},
+                   "sliding_window": args.window, "parallelism": "single-gpu"},
         "step_roofline_ms": t_star * 1e3,
         "step_algorithmic": {"bytes": w_all["bytes"] + w_write["bytes"], "flops": w_all["flops"]},
         "decode": decode, "prefill": prefill,
@@ -222,7 +224,7 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops):
+def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0):
     """The oracle (float64 C, OpenMP) timed on the host on a bounded sample of the same step:
     the full KV write, then attention for every decode row and `n_prefill_rows` prefill rows
     spread evenly over the chunk.  Reported in the metric's unit (the sample's roofline time
@@ -246,9 +248,12 @@ def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops):
         rows = np.nonzero(mask[qsl[r]:qsl[r + 1]])[0]
         if len(rows):
             touched.add(r)
-            flops += 4.0 * batch.num_heads * batch.head_dim * float(np.sum(req.computed + rows + 1))
+            seen = req.computed + rows + 1
+            if window > 0:
+                seen = np.minimum(seen, window)
+            flops += 4.0 * batch.num_heads * batch.head_dim * float(np.sum(seen))
     from workloads.accounting import attention_work
-    kv = attention_work(batch, sorted(touched))["kv_bytes"] if touched else 0.0
+    kv = attention_work(batch, sorted(touched), window=window)["kv_bytes"] if touched else 0.0
     nbytes = kv + int(mask.sum()) * batch.num_heads * batch.head_dim * 2 * (2 if batch.dtype == "bf16" else 4)
     kc, vc = to_np(batch.k_cache).copy(), to_np(batch.v_cache).copy()
     q, k, v = to_np(batch.q), to_np(batch.k), to_np(batch.v)
@@ -256,7 +261,7 @@ def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops):
     t0 = time.perf_counter()
     oracle.kv_write(k, v, batch.slot_mapping.numpy(), kc, vc, batch.dtype, batch.dtype)
     oracle.paged_attention(q, kc, vc, batch.query_start_loc.numpy(), batch.seq_lens.numpy(),
-                           batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=mask)
+                           batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=mask, window=window)
     secs = time.perf_counter() - t0
     t_star = max(nbytes / (PEAK_HBM_GBPS * 1e9), flops / (peak_flops * 1e12))
     eprint(f"[bench] oracle sample: {int(mask.sum())} rows in {secs:.2f}s on {cores} threads")
