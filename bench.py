@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # dense bf16 matrix cores
 PEAK_F32_TFLOPS = 157.3         # fp32 vector
+PREFILL_MIN_COLS = 64           # the library sends requests with more query rows x group heads
+                                # than this to the prefill kernel (bf16, head_dim 128)
 METRIC = "paged-attn decode KV GB/s + prefill TFLOP/s, % of MI355X peak"
 KERNEL_SOURCES = {"prefill": "attn_prefill_mfma.hip", "small": "attn_decode_mfma.hip",
                   "kv_write": "kv_write.hip", "merge": "attn_valu.hip", "plan": "plan.hip"}
@@ -64,7 +66,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context",
-                    choices=["long_context", "decode_only", "shared_prefix", "mixed_step_bf16",
+                    choices=["long_context", "decode_only", "shared_prefix", "spec_verify", "mixed_step_bf16",
                              "mixed_step_f32", "worked_batch"])
     ap.add_argument("--cpu-prefill-rows", type=int, default=256,
                     help="prefill rows in the oracle's timed sample (plus every decode row)")
@@ -149,7 +151,7 @@ def main() -> int:
     g = batch.num_heads // batch.num_kv_heads
     prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim == 128 \
         and 256 % g == 0
-    is_pf = [prefill_capable and r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
+    is_pf = [prefill_capable and r.new * g > PREFILL_MIN_COLS and r.seq_len > 0 for r in batch.requests]
     if kern["prefill"][1] == 0:          # the library routed every request to the small tiles
         is_pf = [False] * len(is_pf)
     pf_ids = [i for i, f in enumerate(is_pf) if f]
@@ -199,7 +201,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         # the oracle's sample is chosen by request shape: every row of requests whose rows times
         # grouped heads fit 16 columns (decodes), and a spread of rows from the longer chunks
-        chunk = [r.new * g > 16 and r.seq_len > 0 for r in batch.requests]
+        chunk = [r.new * g > PREFILL_MIN_COLS and r.seq_len > 0 for r in batch.requests]
         cpu = cpu_baseline(batch, args.cpu_prefill_rows, [i for i, f in enumerate(chunk) if not f],
                            [i for i, f in enumerate(chunk) if f], peak_flops, args.window)
 

@@ -65,9 +65,13 @@ struct alignas(16) ReqOffsets {
   int32_t small, merge, pf, nsplit;
 };
 
-// Classification of request r, identical on host and device.
+// Classification of request r, identical on host and device.  Up to four small tiles (64
+// query columns: decodes, speculative-verification rows, short chunks) stay on the small
+// tiles, whose key splits spread a long context over many workgroups; longer chunks fill
+// the prefill kernel's 256-row tiles.
+constexpr int kPrefillMinCols = 4 * kCols;
 __host__ __device__ __forceinline__ bool use_prefill_path(const Plan& p, int32_t t, int32_t L) {
-  return p.pf_tokens > 0 && L > 0 && t * p.g > kCols;
+  return p.pf_tokens > 0 && L > 0 && (int64_t)t * p.g > kPrefillMinCols;
 }
 // Keys one small tile of a request with context L can see: all L, or with a sliding window
 // of w tokens at most w + tile_tokens - 1 (the tile's rows are consecutive), plus up to 63

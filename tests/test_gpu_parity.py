@@ -96,6 +96,11 @@ def test_shared_prefix_full_size():
     H.check_batch(b, row_mask=_sample_rows(b, 4))
 
 
+def test_spec_verify_full_size():
+    """128 verifications of 1 + k rows (k = 1, 2, 4, 8) over contexts of 512..8192 tokens."""
+    H.check_batch(workloads.spec_verify())
+
+
 def test_long_context_full_size():
     b = workloads.long_context()
     H.check_batch(b, row_mask=_sample_rows(b, 5))

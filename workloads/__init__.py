@@ -279,6 +279,25 @@ def long_context(poison: bool = True, seed: int = 5) -> Batch:
                       description="16 decodes at 32768 + 1 chunk of 4096 at 28672, H=64 Hkv=8 D=128")
 
 
+def spec_verify(poison: bool = True, seed: int = 6, num_reqs: int = 128, min_len: int = 512,
+                max_len: int = 8192) -> Batch:
+    """Speculative verification: every request scores 1 + k new rows (its last accepted
+    token and k draft tokens), k cycling over 1, 2, 4, 8, at seq_len ~ U{512..8192} that
+    includes those rows; bf16, 32/8 heads, D=128, bs=16, pool 1.2x the blocks needed.
+    The verifier's rows are the last t positions of the context like any chunk's."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.randint(min_len, max_len + 1, (num_reqs,), generator=gen).tolist()
+    ks = [(1, 2, 4, 8)[i % 4] for i in range(num_reqs)]
+    reqs = [Request(L - (1 + k), 1 + k) for L, k in zip(lens, ks)]
+    need = sum(-(-L // 16) for L in lens)
+    nb = math.ceil(1.2 * need)
+    assign_blocks(gen, reqs, nb, 16)
+    return make_batch("spec_verify", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison,
+                      description=f"{num_reqs} verifications of 1+k rows, k in (1,2,4,8), seq_len "
+                                  f"U{{{min_len}..{max_len}}}, bf16 H=32 Hkv=8 D=128")
+
+
 CONFIGS = {
     "worked_batch": worked_batch,
     "mixed_step_f32": lambda poison=True: mixed_step("f32", poison),
@@ -286,6 +305,7 @@ CONFIGS = {
     "decode_only": decode_only,
     "shared_prefix": shared_prefix,
     "long_context": long_context,
+    "spec_verify": spec_verify,
 }
 
 
