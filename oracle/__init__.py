@@ -55,6 +55,8 @@ def load_library(path: str):
                                            ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32]
+    lib.oracle_copy_blocks.restype = ctypes.c_int
+    lib.oracle_copy_blocks.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64]
     lib.oracle_round_to_bf16.restype = ctypes.c_uint16
     lib.oracle_round_to_bf16.argtypes = [ctypes.c_double]
     return lib
@@ -100,6 +102,25 @@ def kv_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache: np
                                 n, hkv, d, num_slots, DTYPES[in_dtype], DTYPES[cache_dtype])
     if rc != 0:
         raise ValueError("oracle kv_write: slot out of range")
+
+
+def copy_blocks(src: np.ndarray, dst: np.ndarray, src_block: np.ndarray, dst_block: np.ndarray) -> None:
+    """swap_out / swap_in / copy-on-write: block dst_block[i] of dst becomes block src_block[i]
+    of src, pairs in order.  src and dst are C-contiguous arrays whose first axis is the block
+    (they may be the same array); dst is modified in place."""
+    if not (src.flags.c_contiguous and dst.flags.c_contiguous):
+        raise ValueError("src and dst must be C-contiguous")
+    bb = src.nbytes // src.shape[0]
+    if dst.nbytes // dst.shape[0] != bb:
+        raise ValueError("src and dst blocks differ in size")
+    sb = np.ascontiguousarray(src_block, dtype=np.int64)
+    db = np.ascontiguousarray(dst_block, dtype=np.int64)
+    if sb.shape != db.shape:
+        raise ValueError("src_block and dst_block differ in length")
+    if sb.size and (sb.max() >= src.shape[0] or db.max() >= dst.shape[0]):
+        raise ValueError("block id out of range")
+    if _lib().oracle_copy_blocks(_ptr(src), _ptr(dst), _ptr(sb), _ptr(db), sb.size, bb) != 0:
+        raise ValueError("negative block id")
 
 
 def gather_context(cache: np.ndarray, table_row: np.ndarray, length: int, dtype: str) -> np.ndarray:

@@ -12,7 +12,7 @@
  * block_id * block_size + offset, read in logical order) and its grouped-query note
  * (query heads fold contiguously onto KV heads, kv = h / (H / Hkv)).
  *
- * Everything is plain loops in float64, in the order the pages describe:
+ * Everything is plain loops (float64 arithmetic), in the order the pages describe:
  *   write:      for each new token i (increasing), slot = slot_mapping[i], a negative slot
  *               is redirected to the pool's last slot, then the token's Hkv*D row is copied
  *               (cast to the cache dtype) into that slot.
@@ -75,6 +75,26 @@ static void store_elem(void* base, int64_t idx, int dtype, double x) {
 
 /* bfloat16 pattern of a double, exposed so the rounding can be pinned on its own. */
 uint16_t oracle_round_to_bf16(double x) { return round_to_bf16(x); }
+
+/*
+ * Block copies of "Engine v2: one core for every request": swap_out gathers a preempted
+ * request's blocks of each pool tensor into a host copy, swap_in writes a saved copy into
+ * newly allocated blocks (index_copy_ over the pool's blocks), and copy-on-write copies a
+ * shared block into a private one before the step (vllm-lite README, paged KV cache).  One
+ * rule covers all three: for each pair i, in increasing i, the block_bytes bytes of block
+ * src_block[i] of src become block dst_block[i] of dst.  Returns -1 on a negative id.
+ */
+int oracle_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
+                       int64_t num_pairs, int64_t block_bytes) {
+    for (int64_t i = 0; i < num_pairs; ++i)
+        if (src_block[i] < 0 || dst_block[i] < 0) return -1;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const unsigned char* from = (const unsigned char*)src + src_block[i] * block_bytes;
+        unsigned char* to = (unsigned char*)dst + dst_block[i] * block_bytes;
+        for (int64_t b = 0; b < block_bytes; ++b) to[b] = from[b];
+    }
+    return 0;
+}
 
 /*
  * write_kv ("Attention over the pool"): k, v are [N, Hkv, D] in in_dtype; the caches are

@@ -393,6 +393,61 @@ def check_window_covering_context(orc):
         assert np.array_equal(sc.run_oracle(orc, want_f64=False, window=w), ref), w
 
 
+# ------------------------------------------------------------------------------------------
+# block copies (swap out / swap in, copy-on-write), pinned through the attention they serve
+# ------------------------------------------------------------------------------------------
+
+def check_swap_roundtrip_preserves_attention(orc):
+    """Swap a request's blocks out to a staging buffer, poison them, swap the copy into other
+    free blocks and point the table there: the attention output must not move, bit for bit
+    (a wrong block, a partial block or a reversed copy changes it or turns it NaN)."""
+    sc = Scenario([(30, 4), (0, 9), (50, 2)], 8, 2, 8, 4, seed=31, num_blocks=60)
+    ref = sc.run_oracle(orc, want_f64=False)
+    used = {b for tb in sc.tables for b in tb}
+    free = [b for b in range(sc.num_blocks) if b not in used]
+    for r in (0, 2):
+        blocks = np.array(sc.tables[r], np.int64)
+        n = len(blocks)
+        for pool in (sc.k_pool, sc.v_pool):
+            staging = np.zeros((n,) + pool.shape[1:], pool.dtype)
+            orc.copy_blocks(pool, staging, blocks, np.arange(n))
+            pool[blocks] = np.nan
+            new = np.array(free[:n], np.int64)
+            orc.copy_blocks(staging, pool, np.arange(n), new)
+        sc.tables[r] = [int(b) for b in free[:n]]
+        free = free[n:]
+    assert np.array_equal(sc.run_oracle(orc, want_f64=False), ref)
+
+
+def check_copy_on_write(orc):
+    """Two requests alias a prefix block; copy-on-write gives request 1 a private copy and
+    the next write goes there: request 0 still sees the old contents, request 1 the new."""
+    bs = 4
+    sc = Scenario([(10, 1), (7, 1)], 4, 2, 8, bs, seed=32, num_blocks=12)
+    sc.ctx_k[1][:4] = sc.ctx_k[0][:4]
+    sc.ctx_v[1][:4] = sc.ctx_v[0][:4]
+    sc.build_pool()
+    shared = sc.tables[0][0]
+    sc.tables[1][0] = shared
+    before = sc.run_oracle(orc, want_f64=False)
+    used = {b for tb in sc.tables for b in tb}
+    private = next(b for b in range(sc.num_blocks) if b not in used)
+    for pool in (sc.k_pool, sc.v_pool):
+        orc.copy_blocks(pool, pool, np.array([shared]), np.array([private]))
+    sc.tables[1][0] = private
+    assert np.array_equal(sc.run_oracle(orc, want_f64=False), before)      # the copy is exact
+    # request 1 overwrites position 2 of its private block
+    rng = np.random.default_rng(33)
+    kn = rng.standard_normal((1, sc.Hkv, sc.D)).astype(np.float32)
+    vn = rng.standard_normal((1, sc.Hkv, sc.D)).astype(np.float32)
+    orc.kv_write(kn, vn, np.array([private * bs + 2], np.int64), sc.k_pool, sc.v_pool, "f32", "f32")
+    after = sc.run_oracle(orc, want_f64=False)
+    assert np.array_equal(after[0], before[0])                              # the sharer is untouched
+    sc.ctx_k[1][2] = kn[0]
+    sc.ctx_v[1][2] = vn[0]
+    assert _rel_err(after[1:2], sc.dense(1)) < 1e-6 and not np.array_equal(after[1], before[1])
+
+
 def check_padding_rows_zero(orc):
     """Padding rows (seq_len 0, one query row, slot -1) produce zeros, not 0/0."""
     b = workloads.small_batch([(5, 2), (0, 3)], pad_to=5, seed=9)
@@ -529,4 +584,5 @@ ALL_CHECKS = [
     check_padding_rows_zero, check_block_relabelling, check_aliasing, check_batch_composition,
     check_block_size_invariance, check_rejects_bad_metadata, check_window_dense, check_window_sdpa_bf16,
     check_window_one_is_own_v, check_window_zero_query_gives_window_mean, check_window_covering_context,
+    check_swap_roundtrip_preserves_attention, check_copy_on_write,
 ]

@@ -31,6 +31,12 @@ MUTANTS = [
     ("window_one_key_too_many", "? q_pos - window + 1 : 0;", "? q_pos - window : 0;"),
     ("window_ignored", "? q_pos - window + 1 : 0;", "? 0 : 0;"),
     ("window_one_key_too_few", "? q_pos - window + 1 : 0;", "? q_pos - window + 2 : 0;"),
+    ("copy_half_block", "for (int64_t b = 0; b < block_bytes; ++b) to[b] = from[b];",
+     "for (int64_t b = 0; b < block_bytes / 2; ++b) to[b] = from[b];"),
+    ("copy_wrong_destination", "unsigned char* to = (unsigned char*)dst + dst_block[i] * block_bytes;",
+     "unsigned char* to = (unsigned char*)dst + src_block[i] * block_bytes;"),
+    ("copy_pairs_misaligned", "const unsigned char* from = (const unsigned char*)src + src_block[i] * block_bytes;",
+     "const unsigned char* from = (const unsigned char*)src + src_block[i ? i - 1 : 0] * block_bytes;"),
 ]
 
 
