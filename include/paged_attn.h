@@ -67,6 +67,32 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t num_slots, int32_t in_dtype, int32_t cache_dtype, hipStream_t stream);
 
 /*
+ * paged_copy_blocks: the block copies of preemption and prefix sharing, swap_out /
+ * swap_in of "Engine v2: one core for every request" (section "Preemption") and the
+ * copy-on-write of a shared block (vllm-lite README, paged KV cache).
+ *
+ * For every pair i < num_pairs, block dst_block[i] of dst becomes a copy of block
+ * src_block[i] of src, where a block is block_bytes contiguous bytes: for a pool tensor
+ * [num_blocks + 1, block_size, num_kv_heads, head_dim] that is block_size * num_kv_heads *
+ * head_dim * element size.  Call once per pool tensor (K, V).
+ *   swap_out:      src = pool, dst = staging buffer, dst_block = 0 .. n-1
+ *   swap_in:       src = staging buffer, src_block = 0 .. n-1, dst = pool
+ *   copy-on-write: src = dst = pool
+ *   src, dst          device memory, or host memory pinned with hipHostMalloc (reached over
+ *                     PCIe); 16-byte aligned; src has num_src_blocks blocks, dst
+ *                     num_dst_blocks.
+ *   src_block, dst_block  [num_pairs] int64, device-accessible.
+ *   block_bytes       a positive multiple of 16.
+ * Pairs are copied in parallel.  Preconditions (checked only with debug checks on): ids in
+ * range, dst_block entries distinct, and when src == dst no destination is another pair's
+ * source.  Errors: PA_ERR_SHAPE (sizes, alignment), PA_ERR_NULL, PA_ERR_RANGE (debug),
+ * PA_ERR_LAUNCH.  With timing on, the launch is counted as kind PA_KIND_KV_WRITE.
+ */
+int paged_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
+                      int64_t num_pairs, int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks,
+                      hipStream_t stream);
+
+/*
  * paged_attention_workspace_bytes: device workspace paged_attention_varlen needs for this
  * batch (same arguments as there).  Depends only on the host metadata; returns 0 when the
  * arguments are invalid (the attention call would then report why).
@@ -125,15 +151,27 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
  * Options of the _ex entry points; a NULL pointer means all defaults (the plain entry
  * points above).  reserved[] must be zero.
  *
- *   sliding_window  0: a row at position p attends keys 0 .. p.  w > 0: only the last w of
- *                   them, keys max(0, p - w + 1) .. p: the `window` argument of
- *                   ReferenceBackend.forward ("Attention over the pool": a key is allowed
- *                   iff k_pos > q_pos - window).  Blocks wholly before every row's window
- *                   are not read.  Negative values are rejected (PA_ERR_SHAPE).
+ *   sliding_window     0: a row at position p attends keys 0 .. p.  w > 0: only the last w
+ *                      of them, keys max(0, p - w + 1) .. p: the `window` argument of
+ *                      ReferenceBackend.forward ("Attention over the pool": a key is
+ *                      allowed iff k_pos > q_pos - window).  Blocks wholly before every
+ *                      row's window are not read.  Negative values are rejected.
+ *   graph_max_seq_len  0: the launches are sized from seq_lens_host.  M > 0: they are sized
+ *                      for every seq_len = M instead, so one enqueued call (for instance
+ *                      captured in a HIP graph for a batch padded to a fixed shape, pad_to
+ *                      of "Flattened ragged batches") serves any device seq_lens <= M on
+ *                      replay: the work lists are rebuilt on the device from the device
+ *                      seq_lens, and workgroups beyond them exit.  seq_lens_host may then
+ *                      be NULL; query_start_loc_host must still describe the (fixed) rows.
+ *                      Every request must have rows x (num_heads / num_kv_heads) <= 64
+ *                      (decode and verification batches); seq_lens above M are a
+ *                      precondition violation (not checked).  No call made by the library
+ *                      inside such a capture allocates or uses hipMemset.
  */
 typedef struct pa_attention_options {
   int32_t sliding_window;
-  int32_t reserved[7];
+  int32_t graph_max_seq_len;
+  int32_t reserved[6];
 } pa_attention_options;
 
 /* paged_attention_workspace_bytes with options (the workspace depends on the window). */

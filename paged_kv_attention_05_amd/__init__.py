@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
           -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
-EXPORTS = ["paged_kv_write", "paged_attention_varlen", "paged_attention_workspace_bytes",
+EXPORTS = ["paged_kv_write", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
            "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
            "paged_attn_set_timing", "paged_attn_timing_report"]
@@ -36,7 +36,8 @@ _lib = None
 
 class AttentionOptions(ctypes.Structure):
     """pa_attention_options of the C ABI."""
-    _fields_ = [("sliding_window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("sliding_window", ctypes.c_int32), ("graph_max_seq_len", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class PagedAttnError(RuntimeError):
@@ -56,6 +57,8 @@ def load_library(path: str = LIB_PATH):
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, P]
+    lib.paged_copy_blocks.restype = ctypes.c_int
+    lib.paged_copy_blocks.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
     lib.paged_attention_workspace_bytes.restype = SZ
     lib.paged_attention_workspace_bytes.argtypes = [I32, I64, I32, I32, I32, I32, P, P, I32]
     lib.paged_attention_varlen.restype = ctypes.c_int
@@ -149,22 +152,46 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                               PA_DTYPE[k.dtype], PA_DTYPE[k_cache.dtype], _stream(stream)))
 
 
-def _options(sliding_window: int):
+def _options(sliding_window: int, graph_max_seq_len: int = 0):
     opts = AttentionOptions()
     opts.sliding_window = int(sliding_window)
+    opts.graph_max_seq_len = int(graph_max_seq_len)
     return ctypes.byref(opts), opts
+
+
+def paged_copy_blocks(src: torch.Tensor, dst: torch.Tensor, src_block: torch.Tensor, dst_block: torch.Tensor,
+                      stream=None) -> None:
+    """Block dst_block[i] of dst becomes block src_block[i] of src (first axis = block).
+    swap_out: src = pool, dst = (pinned host or device) staging; swap_in: the reverse;
+    copy-on-write: src is dst.  src_block / dst_block are int64 device tensors."""
+    lib = load_library()
+    for name, t in (("src", src), ("dst", dst)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be device memory or pinned host memory")
+    if src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:]:
+        raise ValueError("src and dst blocks differ")
+    if src_block.dtype != torch.int64 or dst_block.dtype != torch.int64 or src_block.shape != dst_block.shape:
+        raise ValueError("src_block and dst_block must be int64 tensors of one length")
+    if src_block.numel() == 0:
+        return
+    block_bytes = src[0].numel() * src.element_size()
+    _check(lib.paged_copy_blocks(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 _dptr(src_block, "src_block"), _dptr(dst_block, "dst_block"), src_block.numel(),
+                                 block_bytes, src.shape[0], dst.shape[0], _stream(stream)))
 
 
 def paged_attention_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                                     query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
-                                    dtype: torch.dtype, sliding_window: int = 0) -> int:
+                                    dtype: torch.dtype, sliding_window: int = 0, graph_max_seq_len: int = 0) -> int:
     lib = load_library()
-    r = len(seq_lens_host)
-    n = int(query_start_loc_host[-1]) if r else 0
-    ref, _keep = _options(sliding_window)
+    r = len(query_start_loc_host) - 1
+    n = int(query_start_loc_host[-1]) if r > 0 else 0
+    ref, _keep = _options(sliding_window, graph_max_seq_len)
+    lens = _host_i32(seq_lens_host) if seq_lens_host is not None else None
     return int(lib.paged_attention_workspace_bytes_ex(r, n, num_heads, num_kv_heads, head_dim, block_size,
-                                                      _host_i32(query_start_loc_host), _host_i32(seq_lens_host),
-                                                      PA_DTYPE[dtype], ref))
+                                                      _host_i32(query_start_loc_host), lens, PA_DTYPE[dtype], ref))
 
 
 def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -173,9 +200,11 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
                            max_query_len: int = 0, max_seq_len: int = 0,
                            workspace: Optional[torch.Tensor] = None, stream=None,
-                           sliding_window: int = 0) -> torch.Tensor:
+                           sliding_window: int = 0, graph_max_seq_len: int = 0) -> torch.Tensor:
     """Causal attention of the flattened batch over the pool; returns out [N, H, D].
-    sliding_window > 0 limits the row at position p to keys p - sliding_window + 1 .. p."""
+    sliding_window > 0 limits the row at position p to keys p - sliding_window + 1 .. p.
+    graph_max_seq_len > 0 sizes the launches for any device seq_lens up to it (for a call
+    captured in a graph and replayed as the contexts grow); seq_lens_host may be None."""
     lib = load_library()
     n, h, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[1] != block_size or k_cache.shape[3] != d:
@@ -188,9 +217,10 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if out is None:
         out = torch.empty_like(q)
     hkv = k_cache.shape[2]
-    r = len(seq_lens_host)
-    qh, sh = _host_i32(query_start_loc_host), _host_i32(seq_lens_host)
-    ref, _keep = _options(sliding_window)
+    r = len(query_start_loc_host) - 1
+    qh = _host_i32(query_start_loc_host)
+    sh = _host_i32(seq_lens_host) if seq_lens_host is not None else None
+    ref, _keep = _options(sliding_window, graph_max_seq_len)
     need = lib.paged_attention_workspace_bytes_ex(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype], ref)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)

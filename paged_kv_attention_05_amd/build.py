@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpagedattn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "kv_write.hip", "plan.hip", "attn_valu.hip", "attn_decode_mfma.hip",
+SOURCES = ["api.cpp", "kv_write.hip", "block_copy.hip", "plan.hip", "attn_valu.hip", "attn_decode_mfma.hip",
            "attn_prefill_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Per-file extra flags.  The prefill kernel never carries NaN through its arithmetic (keys

@@ -63,19 +63,30 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Options of the _ex entry points (NULL: defaults).  Reserved fields must be zero.
-int read_options(const pa_attention_options* o, int32_t* window) {
+int read_options(const pa_attention_options* o, int32_t* window, int32_t* graph_max) {
   *window = 0;
+  *graph_max = 0;
   if (!o) return PA_OK;
   for (int32_t x : o->reserved)
     if (x != 0) return fail(PA_ERR_SHAPE, "pa_attention_options.reserved must be zero");
   if (o->sliding_window < 0) return fail(PA_ERR_SHAPE, "sliding_window must be >= 0");
+  if (o->graph_max_seq_len < 0) return fail(PA_ERR_SHAPE, "graph_max_seq_len must be >= 0");
   *window = o->sliding_window;
+  *graph_max = o->graph_max_seq_len;
   return PA_OK;
 }
 
 // Validates the host metadata and builds the plan.  Returns PA_OK or an error code.
 int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t bs, int32_t stride,
-              const int32_t* qsl, const int32_t* lens, int32_t dtype, int32_t window, pa::Plan* out) {
+              const int32_t* qsl, const int32_t* lens_host, int32_t dtype, int32_t window, int32_t graph_max,
+              pa::Plan* out) {
+  // with graph_max the launches are sized as if every seq_len were graph_max
+  std::vector<int32_t> capacity;
+  const int32_t* lens = lens_host;
+  if (graph_max > 0 && R > 0) {
+    capacity.assign((size_t)R, graph_max);
+    lens = capacity.data();
+  }
   if (R < 0 || N < 0) return fail(PA_ERR_METADATA, "num_reqs and num_tokens must be >= 0");
   if (N > INT32_MAX) return fail(PA_ERR_SHAPE, "num_tokens must fit in int32");
   if (H <= 0 || Hkv <= 0 || H % Hkv != 0)
@@ -95,6 +106,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   pa::Plan p{};
   p.R = R; p.H = H; p.Hkv = Hkv; p.g = H / Hkv; p.D = D; p.bs = bs;
   p.window = window;
+  if (graph_max > 0)
+    for (int32_t r = 0; r < R; ++r)
+      if ((int64_t)(qsl[r + 1] - qsl[r]) * p.g > pa::kPrefillMinCols)
+        return fail(PA_ERR_SHAPE, "graph_max_seq_len: request " + std::to_string(r) +
+                                      " has more than 64 query columns (rows x group heads)");
   if (p.g >= pa::kCols) { p.tile_heads = pa::kCols; p.tile_tokens = 1; }
   else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
   p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
@@ -216,6 +232,38 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, vo
   return PA_OK;
 }
 
+int paged_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
+                      int64_t num_pairs, int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks,
+                      hipStream_t stream) {
+  g_last_error.clear();
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs must be >= 0");
+  if (block_bytes <= 0 || block_bytes % 16 != 0) return fail(PA_ERR_SHAPE, "block_bytes must be a positive multiple of 16");
+  if (num_pairs == 0) return PA_OK;
+  if (!src || !dst || !src_block || !dst_block) return fail(PA_ERR_NULL, "null pointer argument");
+  if (!aligned16(src) || !aligned16(dst)) return fail(PA_ERR_SHAPE, "src and dst must be 16-byte aligned");
+  if (g_debug_checks) {
+    std::vector<int64_t> sb((size_t)num_pairs), db((size_t)num_pairs);
+    if (hipMemcpy(sb.data(), src_block, 8 * sb.size(), hipMemcpyDefault) != hipSuccess ||
+        hipMemcpy(db.data(), dst_block, 8 * db.size(), hipMemcpyDefault) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "debug check: copy of the block ids failed");
+    std::unordered_set<int64_t> dsts;
+    for (size_t i = 0; i < sb.size(); ++i) {
+      if (sb[i] < 0 || sb[i] >= num_src_blocks) return fail(PA_ERR_RANGE, "src_block[" + std::to_string(i) + "] out of range");
+      if (db[i] < 0 || db[i] >= num_dst_blocks) return fail(PA_ERR_RANGE, "dst_block[" + std::to_string(i) + "] out of range");
+      if (!dsts.insert(db[i]).second) return fail(PA_ERR_RANGE, "dst_block[" + std::to_string(i) + "] repeats a block");
+    }
+    if (src == dst)
+      for (size_t i = 0; i < sb.size(); ++i)
+        if (dsts.count(sb[i]) && db[i] != sb[i])
+          return fail(PA_ERR_RANGE, "src_block[" + std::to_string(i) + "] is also a destination");
+  }
+  const hipError_t e = timed(PA_KIND_KV_WRITE, stream, [&] {
+    return pa::launch_copy_blocks(src, dst, src_block, dst_block, num_pairs, block_bytes, stream);
+  });
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("block copy launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                        const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
@@ -230,11 +278,11 @@ size_t paged_attention_workspace_bytes_ex(int32_t num_reqs, int64_t num_tokens, 
                                           int32_t dtype, const pa_attention_options* options) {
   pa::Plan p;
   const std::string keep = g_last_error;
-  int32_t window = 0;
-  int rc = read_options(options, &window);
+  int32_t window = 0, graph_max = 0;
+  int rc = read_options(options, &window, &graph_max);
   if (rc == PA_OK)
     rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, INT32_MAX,
-                   query_start_loc_host, seq_lens_host, dtype, window, &p);
+                   query_start_loc_host, seq_lens_host, dtype, window, graph_max, &p);
   g_last_error = keep;
   return rc == PA_OK ? p.total_bytes : 0;
 }
@@ -267,12 +315,12 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   (void)max_query_len;
   (void)max_seq_len;
   if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
-  int32_t window = 0;
-  int rc = read_options(options, &window);
+  int32_t window = 0, graph_max = 0;
+  int rc = read_options(options, &window, &graph_max);
   if (rc != PA_OK) return rc;
   pa::Plan p;
   rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                 query_start_loc_host, seq_lens_host, dtype, window, &p);
+                 query_start_loc_host, seq_lens_host, dtype, window, graph_max, &p);
   if (rc != PA_OK) return rc;
   if (num_reqs == 0) return PA_OK;
   if (!query_start_loc || !seq_lens || !block_table || !workspace) return fail(PA_ERR_NULL, "null pointer argument");
@@ -284,7 +332,7 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   if (workspace_bytes < p.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.total_bytes) + " bytes");
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
-  if (g_debug_checks) {
+  if (g_debug_checks && graph_max == 0) {   // (sized-for-capacity calls may be captured: no sync)
     std::vector<int32_t> tb((size_t)num_reqs * block_table_stride);
     if (!tb.empty() && hipMemcpy(tb.data(), block_table, sizeof(int32_t) * tb.size(), hipMemcpyDeviceToHost) != hipSuccess)
       return fail(PA_ERR_LAUNCH, "debug check: copy of block_table failed");
@@ -305,6 +353,7 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   a.g = p.g; a.D = head_dim; a.tile_tokens = p.tile_tokens; a.tile_heads = p.tile_heads;
   a.split_keys = p.split_keys;
   a.window = p.window;
+  a.totals = (const int32_t*)((const char*)workspace + p.off_req + sizeof(pa::ReqOffsets) * (size_t)num_reqs);
   a.scale_log2e = scale * 1.4426950408889634f;
 
   hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });

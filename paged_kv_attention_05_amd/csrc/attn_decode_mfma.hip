@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
 
   const int32_t item = blockIdx.x;
   const int hkv = blockIdx.y;
+  if (item >= __builtin_amdgcn_readfirstlane(a.totals[0])) return;
   SmallItem it = items[item];
   // the item is the same for the whole workgroup: scalar registers, scalar loop bounds
   it.r = __builtin_amdgcn_readfirstlane(it.r);

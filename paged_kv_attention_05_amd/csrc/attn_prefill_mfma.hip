@@ -136,6 +136,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     if (__builtin_amdgcn_readfirstlane(wide[lin]) == 0) return;   // the fast kernel's output stands
   }
   const int hkv = lin / n_items;
+  if (lin - hkv * n_items >= __builtin_amdgcn_readfirstlane(a.totals[2])) return;
   const PfItem it = items[lin - hkv * n_items];
 
   const int tid = threadIdx.x;

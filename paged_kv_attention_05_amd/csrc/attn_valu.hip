@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
   __shared__ float sP[4][16][kCols + 1];   // per wave: P[key][column]
   __shared__ float sM[4][kCols], sL[4][kCols], sTot[kCols], sMax[kCols];
 
+  if ((int32_t)blockIdx.x >= __builtin_amdgcn_readfirstlane(a.totals[0])) return;
   const SmallItem it = items[blockIdx.x];
   const int hkv = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(256) void merge_splits(AttnArgs a, const MergeItem*
                                                     Partials part) {
   const int D = a.D;
   const int cols_per_wg = 256 / D;
+  if ((int32_t)(blockIdx.x / a.Hkv) >= __builtin_amdgcn_readfirstlane(a.totals[1])) return;
   const int hkv = blockIdx.x % a.Hkv;
   const MergeItem it = items[blockIdx.x / a.Hkv];
   const int col = blockIdx.y * cols_per_wg + threadIdx.x / D;

@@ -122,6 +122,10 @@ struct AttnArgs {
   int32_t window;                    // sliding window in tokens: a row at position p sees keys
                                      // p - window + 1 .. p; 0: keys 0 .. p
   float scale_log2e;                 // scale * log2(e): scores are kept in base 2
+  // {small, merge, prefill} item counts the planner kernel wrote for this call (workspace).
+  // Grids are sized on the host; a workgroup past the device count exits (the counts agree
+  // except when a captured graph replays with shorter contexts than it was sized for).
+  const int32_t* totals;
 };
 
 struct Partials {
@@ -135,6 +139,8 @@ hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, v
                            int64_t n, int32_t row_elems, int64_t num_slots, int32_t in_dtype,
                            int32_t cache_dtype, hipStream_t s);
 hipError_t launch_plan(const Plan& p, const int32_t* qsl, const int32_t* seq_lens, void* ws, hipStream_t s);
+hipError_t launch_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
+                              int64_t num_pairs, int64_t block_bytes, hipStream_t s);
 hipError_t launch_small_valu(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
 hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);

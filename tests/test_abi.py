@@ -114,3 +114,28 @@ def test_window_shrinks_the_split_workspace():
     assert 0 < windowed < full
     opts.sliding_window = 0
     assert lib.paged_attention_workspace_bytes_ex(2, 2, 8, 2, 128, 16, qsl, lens, 1, ctypes.byref(opts)) == full
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    lib = pk.load_library()
+    assert lib.paged_copy_blocks(FAKE, FAKE, FAKE, FAKE, 3, 100, 8, 8, None) == -2     # not a multiple of 16
+    assert lib.paged_copy_blocks(FAKE, FAKE, FAKE, FAKE, -1, 64, 8, 8, None) == -2     # negative count
+    assert lib.paged_copy_blocks(None, FAKE, FAKE, FAKE, 3, 64, 8, 8, None) == -1
+    assert lib.paged_copy_blocks(ctypes.c_void_p(0x1008), FAKE, FAKE, FAKE, 3, 64, 8, 8, None) == -2   # misaligned
+    assert lib.paged_copy_blocks(None, None, None, None, 0, 64, 0, 0, None) == 0        # nothing to copy
+
+
+def test_graph_sizing():
+    """Sized for capacity: host seq_lens may be absent; chunks over 64 query columns are
+    refused (their routing could change with the device lengths)."""
+    lib = pk.load_library()
+    opts = pk.AttentionOptions()
+    opts.graph_max_seq_len = 4096
+    ok = lib.paged_attention_workspace_bytes_ex(3, 3, 32, 8, 128, 16, _host([0, 1, 2, 3]), None, 1, ctypes.byref(opts))
+    assert ok > 0
+    long_chunk = lib.paged_attention_workspace_bytes_ex(2, 40, 32, 8, 128, 16, _host([0, 1, 40]), None, 1,
+                                                        ctypes.byref(opts))
+    assert long_chunk == 0
+    opts.graph_max_seq_len = -1
+    assert lib.paged_attention_workspace_bytes_ex(3, 3, 32, 8, 128, 16, _host([0, 1, 2, 3]), None, 1,
+                                                  ctypes.byref(opts)) == 0

@@ -141,6 +141,165 @@ def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     H.check_batch(b, label=name)
 
 
+# ------------------------------------------------------------------------- block copies
+@pytest.mark.parametrize("dtype,shape", [("bf16", (41, 16, 8, 128)), ("f32", (23, 16, 4, 48)), ("bf16", (25, 1, 1, 8))],
+                         ids=["bf16_d128", "f32_d48", "bf16_tiny_block"])
+def test_copy_blocks_parity(dtype, shape):
+    """swap_out to device and to pinned host staging, swap_in from pinned host, and
+    copy-on-write inside the pool: every byte as the oracle's copy."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(51)
+    pool = torch.randn(shape, generator=gen).to(workloads.TORCH_DTYPES[dtype])
+    nb = shape[0]
+    perm = torch.randperm(nb, generator=gen)
+    out_ids, in_ids = perm[:7].to(torch.int64), perm[7:14].to(torch.int64)
+    cow_src, cow_dst = perm[14:17].to(torch.int64), perm[17:20].to(torch.int64)
+    n = len(out_ids)
+    ref = to_np(pool).copy()
+    gpu = pool.to(dev)
+    # swap_out: pool -> device staging and pool -> pinned host staging
+    st_dev = torch.zeros((n,) + shape[1:], dtype=pool.dtype, device=dev)
+    st_host = torch.zeros((n,) + shape[1:], dtype=pool.dtype).pin_memory()
+    seq = torch.arange(n, dtype=torch.int64)
+    pk.paged_copy_blocks(gpu, st_dev, out_ids.to(dev), seq.to(dev))
+    pk.paged_copy_blocks(gpu, st_host, out_ids.to(dev), seq.to(dev))
+    torch.cuda.synchronize()
+    want_st = np.zeros((n,) + ref.shape[1:], ref.dtype)
+    oracle.copy_blocks(ref, want_st, out_ids.numpy(), seq.numpy())
+    assert np.array_equal(to_np(st_dev.cpu()).view(np.uint8), want_st.view(np.uint8))
+    assert np.array_equal(to_np(st_host).view(np.uint8), want_st.view(np.uint8))
+    # swap_in: pinned host staging -> other blocks of the pool; then copy-on-write pairs
+    pk.paged_copy_blocks(st_host, gpu, seq.to(dev), in_ids.to(dev))
+    pk.paged_copy_blocks(gpu, gpu, cow_src.to(dev), cow_dst.to(dev))
+    torch.cuda.synchronize()
+    oracle.copy_blocks(want_st, ref, seq.numpy(), in_ids.numpy())
+    oracle.copy_blocks(ref, ref, cow_src.numpy(), cow_dst.numpy())
+    assert np.array_equal(to_np(gpu.cpu()).view(np.uint8), ref.view(np.uint8))
+
+
+def test_swap_round_trip_keeps_attention():
+    """Swap a prefill request's and a decode's blocks out to pinned host memory, poison them,
+    swap them into free blocks and remap the tables: the GPU output is bit-identical."""
+    import paged_kv_attention_05_amd as pk
+    dev = torch.device("cuda:0")
+    b = workloads.small_batch([(700, 150), (3000, 1), (40, 1)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=52, num_blocks=600)
+    ref, kc, vc = H.gpu_step(b)
+    used = {x for r in b.requests for x in r.blocks}
+    free = [x for x in range(b.num_blocks) if x not in used]
+    table = b.block_table.clone()
+    kc, vc = kc.to(dev), vc.to(dev)
+    for r in (0, 1):
+        blocks = torch.tensor(b.requests[r].blocks, dtype=torch.int64)
+        n = len(blocks)
+        new = torch.tensor(free[:n], dtype=torch.int64)
+        free = free[n:]
+        seq = torch.arange(n, dtype=torch.int64, device=dev)
+        for pool in (kc, vc):
+            host = torch.empty((n,) + tuple(pool.shape[1:]), dtype=pool.dtype).pin_memory()
+            pk.paged_copy_blocks(pool, host, blocks.to(dev), seq)
+            torch.cuda.synchronize()
+            pool[blocks.to(dev)] = float("nan")
+            pk.paged_copy_blocks(host, pool, seq, new.to(dev))
+        table[r, :n] = new.to(torch.int32)
+    out = pk.paged_attention_varlen(b.q.to(dev), kc, vc, b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                    table.to(dev), b.block_size, b.scale,
+                                    query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+def test_copy_blocks_debug_checks():
+    import paged_kv_attention_05_amd as pk
+    dev = torch.device("cuda:0")
+    pool = torch.zeros((8, 16, 2, 64), dtype=torch.bfloat16, device=dev)
+    pk.set_debug_checks(True)
+    try:
+        with pytest.raises(pk.PagedAttnError) as e:
+            pk.paged_copy_blocks(pool, pool, torch.tensor([1, 2], device=dev), torch.tensor([3, 3], device=dev))
+        assert e.value.code == -7
+        with pytest.raises(pk.PagedAttnError):
+            pk.paged_copy_blocks(pool, pool, torch.tensor([1], device=dev), torch.tensor([8], device=dev))
+        with pytest.raises(pk.PagedAttnError):      # 2 is a destination and another pair's source
+            pk.paged_copy_blocks(pool, pool, torch.tensor([1, 2], device=dev), torch.tensor([2, 5], device=dev))
+    finally:
+        pk.set_debug_checks(False)
+
+
+# ------------------------------------------------------------------------- graph capture
+def test_graph_captured_decode_step_replays():
+    """A padded decode batch (13 requests + 3 padding rows, pad_to of "Flattened ragged
+    batches") captured once in a HIP graph as KV write + attention sized for seq_len <= 2048,
+    then replayed on four batches with other lengths, tables and values copied into the
+    captured buffers.  Every replay matches the oracle, and the same call made eagerly with
+    the same sizing gives the same bits; eager work and synchronisations run between replays."""
+    import paged_kv_attention_05_amd as pk
+    dev = torch.device("cuda:0")
+    MAX, NB, R, W = 2048, 2100, 16, 2048 // 16
+    rng = np.random.default_rng(61)
+
+    def batch(seed):
+        lens = rng.integers(1, MAX, size=13)
+        return workloads.small_batch([(int(L) - 1, 1) for L in lens], dtype="bf16", num_heads=32, num_kv_heads=8,
+                                     head_dim=128, num_blocks=NB, seed=seed, pad_to=R)
+
+    def table_of(b):
+        t = torch.zeros((R, W), dtype=torch.int32)
+        t[:, :b.block_table.shape[1]] = b.block_table
+        return t
+
+    b0 = batch(100)
+    st = {"q": b0.q.to(dev), "k": b0.k.to(dev), "v": b0.v.to(dev), "slots": b0.slot_mapping.to(dev),
+          "qsl": b0.query_start_loc.to(dev), "lens": b0.seq_lens.to(dev), "table": table_of(b0).to(dev),
+          "kc": b0.k_cache.to(dev), "vc": b0.v_cache.to(dev)}
+    out = torch.empty_like(st["q"])
+    qsl_host = b0.query_start_loc_host
+    need = pk.paged_attention_workspace_bytes(32, 8, 128, 16, qsl_host, None, torch.bfloat16, graph_max_seq_len=MAX)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step(o, kc, vc, wsp):
+        pk.paged_kv_write(st["k"], st["v"], st["slots"], kc, vc)
+        pk.paged_attention_varlen(st["q"], kc, vc, st["qsl"], st["lens"], st["table"], 16, b0.scale, o,
+                                  query_start_loc_host=qsl_host, seq_lens_host=None, workspace=wsp,
+                                  graph_max_seq_len=MAX)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out, st["kc"], st["vc"], ws)            # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out, st["kc"], st["vc"], ws)
+
+    for i in range(4):
+        b = batch(200 + i)
+        assert b.query_start_loc_host == qsl_host
+        for key, src in (("q", b.q), ("k", b.k), ("v", b.v), ("slots", b.slot_mapping), ("qsl", b.query_start_loc),
+                         ("lens", b.seq_lens), ("table", table_of(b)), ("kc", b.k_cache), ("vc", b.v_cache)):
+            st[key].copy_(src.to(dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu()
+        # eager: the same sizing on fresh caches and workspace, then the oracle
+        kc2, vc2 = b.k_cache.to(dev), b.v_cache.to(dev)
+        out2 = torch.empty_like(st["q"])
+        ws2 = torch.empty_like(ws)
+        step(out2, kc2, vc2, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), out2.cpu().view(torch.int16)), i
+        assert torch.equal(st["kc"].cpu().view(torch.int16)[:-1], kc2.cpu().view(torch.int16)[:-1])
+        ref64, _, _ = H.oracle_step(b)
+        err = attention_error(got.float().numpy(), ref64, "bf16")
+        H.log(f"[parity] graph replay {i}: error {err:.3g} x bound")
+        assert err <= 1.0, (i, err)
+
+
 # ------------------------------------------------------------------------- sliding window
 WINDOW = [
     # (name, specs (computed, new), H, Hkv, D, bs, dtype, windows)
