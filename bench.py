@@ -67,12 +67,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context",
                     choices=["long_context", "decode_only", "shared_prefix", "spec_verify", "mixed_step_bf16",
-                             "mixed_step_f32", "worked_batch"])
+                             "mixed_step_f32", "worked_batch", "small_decode", "block_copy"])
     ap.add_argument("--cpu-prefill-rows", type=int, default=256,
                     help="prefill rows in the oracle's timed sample (plus every decode row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (0: none); the workload is otherwise unchanged")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step once in a HIP graph (launches sized for the batch's max seq_len) "
+                         "and time graph replays; per-kernel times still come from eager steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once: a plain copy "
                          "of known size whose HBM counters scale the kernels' counters")
@@ -97,6 +100,8 @@ def main() -> int:
         return 1
     pk.load_library()
     dev = torch.device("cuda:0")
+    if args.workload == "block_copy":
+        return bench_block_copy(args, torch, pk, dev)
 
     t0 = time.time()
     batch = workloads.CONFIGS[args.workload](poison=False)
@@ -112,12 +117,23 @@ def main() -> int:
                                                   batch.seq_lens_host, q.dtype, sliding_window=args.window)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
+    graph_max = batch.max_seq_len if args.graph else 0
+    if args.graph:
+        ws_bytes = pk.paged_attention_workspace_bytes(batch.num_heads, batch.num_kv_heads, batch.head_dim,
+                                                      batch.block_size, batch.query_start_loc_host, None, q.dtype,
+                                                      sliding_window=args.window, graph_max_seq_len=graph_max)
+        if ws_bytes == 0:
+            eprint("--graph needs every request to have at most 64 query columns (decode-like batches)")
+            return 2
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
     def step():
         pk.paged_kv_write(k, v, slots, kc, vc)
         pk.paged_attention_varlen(q, kc, vc, qsl, lens, table, batch.block_size, batch.scale, out,
                                   query_start_loc_host=batch.query_start_loc_host,
                                   seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
-                                  max_seq_len=batch.max_seq_len, workspace=ws, sliding_window=args.window)
+                                  max_seq_len=batch.max_seq_len, workspace=ws, sliding_window=args.window,
+                                  graph_max_seq_len=graph_max)
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -143,6 +159,27 @@ def main() -> int:
     ms_per_step = start.elapsed_time(end) / args.steps
     kern = pk.timing_report()
     pk.set_timing(False)
+    eager_ms = ms_per_step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(end) / args.steps
+        eprint(f"[bench] graph replays: {ms_per_step:.4f} ms/step (eager {eager_ms:.4f})")
     kern_avg = {name: (tot / cnt if cnt else 0.0) for name, (tot, cnt) in kern.items()}
     eprint(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernels (avg ms): "
            + ", ".join(f"{n}={t:.4f}" for n, t in kern_avg.items() if t))
@@ -212,16 +249,67 @@ def main() -> int:
         "config": {"workload": batch.name, "description": batch.description, "num_tokens": batch.num_tokens,
                    "num_reqs": batch.num_reqs, "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
                    "head_dim": batch.head_dim, "block_size": batch.block_size, "pool_blocks": batch.num_blocks,
-                   "sliding_window": args.window, "parallelism": "single-gpu"},
+                   "sliding_window": args.window, "launch": "hip_graph" if args.graph else "eager",
+                   "parallelism": "single-gpu"},
         "step_roofline_ms": t_star * 1e3,
         "step_algorithmic": {"bytes": w_all["bytes"] + w_write["bytes"], "flops": w_all["flops"]},
         "decode": decode, "prefill": prefill,
         "kv_write": {"avg_ms": kern_avg["kv_write"], "bytes": w_write["bytes"],
                      "gbps": w_write["bytes"] / (kern_avg["kv_write"] * 1e-3) / 1e9 if kern_avg["kv_write"] else None},
         "kernels_avg_ms": kern_avg,
+        "eager_ms_per_step": eager_ms,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_block_copy(args, torch, pk, dev):
+    """Block copies of preemption and prefix sharing, on the pool of the long-context batch's
+    shape (bf16, 8 KV heads x 128, 16-token blocks: 32 KiB per block and tensor): swap one
+    32768-token request (2048 blocks of K and of V) out to pinned host memory and back into
+    other blocks, and copy-on-write 1024 blocks inside the pool.  Swaps are bound by PCIe,
+    copy-on-write by HBM (read + write)."""
+    nb, n_swap, n_cow = 40001, 2048, 1024
+    gen = torch.Generator().manual_seed(7)
+    pools = [torch.randn((nb, 16, 8, 128), generator=gen).to(torch.bfloat16).to(dev) for _ in range(2)]
+    perm = torch.randperm(nb - 1, generator=gen)
+    out_ids, in_ids = perm[:n_swap].to(dev), perm[n_swap:2 * n_swap].to(dev)
+    cow_src, cow_dst = perm[2 * n_swap:2 * n_swap + n_cow].to(dev), perm[2 * n_swap + n_cow:2 * n_swap + 2 * n_cow].to(dev)
+    seq = torch.arange(n_swap, dtype=torch.int64, device=dev)
+    host = [torch.empty((n_swap, 16, 8, 128), dtype=torch.bfloat16).pin_memory() for _ in range(2)]
+    block_bytes = 16 * 8 * 128 * 2
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_out = timed(lambda: [pk.paged_copy_blocks(p, h, out_ids, seq) for p, h in zip(pools, host)])
+    ms_in = timed(lambda: [pk.paged_copy_blocks(h, p, seq, in_ids) for p, h in zip(pools, host)])
+    ms_cow = timed(lambda: [pk.paged_copy_blocks(p, p, cow_src, cow_dst) for p in pools])
+    swap_bytes = 2 * n_swap * block_bytes
+    cow_bytes = 2 * n_cow * block_bytes * 2                      # read + write
+    cow_gbps = cow_bytes / (ms_cow * 1e-3) / 1e9
+    line = {"metric": "block copy GB/s (copy-on-write in HBM, swap over PCIe)", "value": cow_gbps, "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_cow, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "block_copy", "pool_blocks": nb, "block_bytes_per_tensor": block_bytes,
+                       "swap_blocks": n_swap, "cow_pairs": n_cow, "tensors": 2, "parallelism": "single-gpu"},
+            "copy_on_write": {"ms": ms_cow, "hbm_bytes": cow_bytes, "gbps": cow_gbps},
+            "swap_out_to_pinned_host": {"ms": ms_out, "bytes": swap_bytes, "gbps": swap_bytes / (ms_out * 1e-3) / 1e9},
+            "swap_in_from_pinned_host": {"ms": ms_in, "bytes": swap_bytes, "gbps": swap_bytes / (ms_in * 1e-3) / 1e9},
+            "roofline": {"kernel": "copy_blocks16", "bound": "hbm", "achieved": cow_gbps, "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": cow_gbps / PEAK_HBM_GBPS, "traffic": None},
+            "cpu_baseline": None}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -298,6 +298,21 @@ def spec_verify(poison: bool = True, seed: int = 6, num_reqs: int = 128, min_len
                                   f"U{{{min_len}..{max_len}}}, bf16 H=32 Hkv=8 D=128")
 
 
+def small_decode(poison: bool = True, seed: int = 7) -> Batch:
+    """A decode batch of 13 requests padded to 16 rows (pad_to of "Flattened ragged
+    batches": three rows with slot -1 and seq_len 0, the shape a captured graph serves),
+    seq_len ~ U{256..2048}, bf16, 32/8 heads, D=128, bs=16, pool 1.2x the blocks needed."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.randint(256, 2049, (13,), generator=gen).tolist()
+    reqs = [Request(L - 1, 1) for L in lens]
+    need = sum(-(-L // 16) for L in lens)
+    nb = math.ceil(1.2 * need)
+    assign_blocks(gen, reqs, nb, 16)
+    return make_batch("small_decode", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, pad_to=16,
+                      description="13 decodes padded to 16 rows, seq_len U{256..2048}, bf16 H=32 Hkv=8 D=128")
+
+
 CONFIGS = {
     "worked_batch": worked_batch,
     "mixed_step_f32": lambda poison=True: mixed_step("f32", poison),
@@ -306,6 +321,7 @@ CONFIGS = {
     "shared_prefix": shared_prefix,
     "long_context": long_context,
     "spec_verify": spec_verify,
+    "small_decode": small_decode,
 }
 
 
