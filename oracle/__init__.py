@@ -54,7 +54,14 @@ def load_library(path: str):
     lib.oracle_paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_double, P, P,
                                            ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32]
+                                           ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.oracle_kv_write_fp8.restype = ctypes.c_int
+    lib.oracle_kv_write_fp8.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
     lib.oracle_copy_blocks.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64]
     lib.oracle_round_to_bf16.restype = ctypes.c_uint16
@@ -104,6 +111,34 @@ def kv_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache: np
         raise ValueError("oracle kv_write: slot out of range")
 
 
+def fp8_e4m3_encode(y: float) -> int:
+    """Nearest fp8 E4M3 (OCP FN) code of a float32 value, ties to even, saturating at 448."""
+    return int(_lib().oracle_fp8_e4m3_encode(float(np.float32(y))))
+
+
+def fp8_e4m3_decode(code: int) -> float:
+    return float(_lib().oracle_fp8_e4m3_decode(int(code)))
+
+
+def kv_write_fp8(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 k_scale: np.ndarray, v_scale: np.ndarray, in_dtype: str) -> None:
+    """write_kv into quantized pools: codes into k_cache / v_cache ([NB+1, bs, Hkv, D] uint8),
+    scales into k_scale / v_scale ([NB+1, bs, Hkv] float32); negative slots go to the last."""
+    _check_data(k, in_dtype, "k")
+    _check_data(v, in_dtype, "v")
+    for name, a, dt in (("k_cache", k_cache, np.uint8), ("v_cache", v_cache, np.uint8),
+                        ("k_scale", k_scale, np.float32), ("v_scale", v_scale, np.float32)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise TypeError(f"{name}: expected C-contiguous {np.dtype(dt).name}")
+    slot_mapping = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    n, hkv, d = k.shape
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    rc = _lib().oracle_kv_write_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(k_scale), _ptr(v_scale), n, hkv, d, num_slots, DTYPES[in_dtype])
+    if rc != 0:
+        raise ValueError("oracle kv_write_fp8: slot out of range")
+
+
 def copy_blocks(src: np.ndarray, dst: np.ndarray, src_block: np.ndarray, dst_block: np.ndarray) -> None:
     """swap_out / swap_in / copy-on-write: block dst_block[i] of dst becomes block src_block[i]
     of src, pairs in order.  src and dst are C-contiguous arrays whose first axis is the block
@@ -136,7 +171,8 @@ def gather_context(cache: np.ndarray, table_row: np.ndarray, length: int, dtype:
 def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                     query_start_loc: np.ndarray, seq_lens: np.ndarray, block_table: np.ndarray,
                     scale: float, dtype: str, row_mask: Optional[np.ndarray] = None,
-                    want_f64: bool = False, window: int = 0):
+                    want_f64: bool = False, window: int = 0, k_scale: Optional[np.ndarray] = None,
+                    v_scale: Optional[np.ndarray] = None):
     """ReferenceBackend.forward over the pool.
 
     q [N, H, D]; caches [NB+1, bs, Hkv, D]; query_start_loc [R+1]; seq_lens [R];
@@ -145,10 +181,22 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     are left at zero (and NaN in the float64 result) so they cannot pass for results.
     window > 0: a row at position p sees only keys p - window + 1 .. p (the sliding window
     of ReferenceBackend.forward); 0 sees every key up to p.
+    With k_scale / v_scale ([NB+1, bs, Hkv] float32) the caches are fp8 E4M3 codes (uint8)
+    and every gathered row is its codes' values times its scale (ReferenceBackend.dequantize).
     """
     _check_data(q, dtype, "q")
-    _check_data(k_cache, dtype, "k_cache")
-    _check_data(v_cache, dtype, "v_cache")
+    fp8 = k_scale is not None
+    if fp8:
+        for name, a in (("k_cache", k_cache), ("v_cache", v_cache)):
+            if a.dtype != np.uint8 or not a.flags.c_contiguous:
+                raise TypeError(f"{name}: expected C-contiguous uint8 fp8 codes")
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+        if k_scale.shape != k_cache.shape[:3] or v_scale.shape != v_cache.shape[:3]:
+            raise ValueError("scales must be [NB+1, bs, Hkv]")
+    else:
+        _check_data(k_cache, dtype, "k_cache")
+        _check_data(v_cache, dtype, "v_cache")
     qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     table = np.ascontiguousarray(block_table, dtype=np.int32)
@@ -161,7 +209,8 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     rc = _lib().oracle_paged_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(qsl), _ptr(lens),
                                        _ptr(table), bs, float(scale), _ptr(out), _ptr(out64),
                                        len(lens), n, h, hkv, d, table.shape[1], num_slots,
-                                       DTYPES[dtype], _ptr(mask), int(window))
+                                       DTYPES[dtype], _ptr(mask), int(window), 2 if fp8 else DTYPES[dtype],
+                                       _ptr(k_scale), _ptr(v_scale))
     if rc == -1:
         raise ValueError("oracle paged_attention: inconsistent batch metadata")
     if rc != 0:

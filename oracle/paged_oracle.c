@@ -25,8 +25,17 @@
  *               `allowed = k_pos > q_pos - window` states in "Attention over the pool".
  *               Requests with seq_len == 0 or no query rows leave their rows at zero.
  *
- * dtype codes: 0 = float32, 1 = bfloat16 (stored as the upper 16 bits of a float32).
- * Rounding to an output dtype is round-to-nearest-even, done once from float64.
+ * dtype codes: 0 = float32, 1 = bfloat16 (stored as the upper 16 bits of a float32),
+ * 2 = fp8 E4M3 pools with a float32 scale per (slot, KV head).  Rounding to an output dtype
+ * is round-to-nearest-even, done once from float64.
+ *
+ * Quantized pools ("Attention over the pool": ReferenceBackend.dequantize multiplies each
+ * gathered K or V row by its scale, which quantized pools keep beside K and V).  The pages
+ * fix the read side only; the write side taken here is the plainest one that read supports:
+ * per (token, KV head) row, scale = max|x| / 448 (the largest fp8 E4M3 value; 1 for an
+ * all-zero row) and the stored codes are x / scale rounded to the nearest fp8 E4M3 value.
+ * Those two divisions and the max are done in float32, the precision the kernel computes
+ * them in, since they decide the stored codes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -35,6 +44,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_FP8 2
 
 /* Value of element idx of an array of the given dtype, exactly, as a double. */
 static double load_elem(const void* base, int64_t idx, int dtype) {
@@ -75,6 +85,74 @@ static void store_elem(void* base, int64_t idx, int dtype, double x) {
 
 /* bfloat16 pattern of a double, exposed so the rounding can be pinned on its own. */
 uint16_t oracle_round_to_bf16(double x) { return round_to_bf16(x); }
+
+/*
+ * fp8 E4M3, the OCP "FN" variant: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 holds the subnormals m * 2^-9; there are no infinities and S.1111.111 is NaN, so
+ * the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+double oracle_fp8_e4m3_decode(uint8_t b) {
+    const int e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Nearest fp8 E4M3 value to y (ties to even); magnitudes beyond 448 saturate to 448 and NaN
+ * becomes the NaN code.  The value is rounded on the spacing of its binade (2^(E-3) for
+ * |y| in [2^E, 2^(E+1)), E >= -6; 2^-9 below 2^-6), then encoded. */
+uint8_t oracle_fp8_e4m3_encode(float y) {
+    if (isnan(y)) return 0x7F;
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (a == 0.0) return sign;
+    int E;
+    (void)frexp(a, &E);                 /* a = f * 2^E, 0.5 <= f < 1 */
+    E -= 1;                             /* a in [2^E, 2^(E+1)) */
+    const int q = (E < -6 ? -6 : E) - 3;
+    const double r = ldexp(rint(ldexp(a, -q)), q);
+    if (r >= 448.0) return sign | 0x7E;
+    if (r == 0.0) return sign;
+    int Er;
+    (void)frexp(r, &Er);
+    Er -= 1;
+    if (Er < -6) return sign | (uint8_t)ldexp(r, 9);                     /* subnormal: r = m * 2^-9 */
+    return sign | (uint8_t)((Er + 7) << 3) | (uint8_t)(ldexp(r, -Er) * 8.0 - 8.0);
+}
+
+/* One (token, KV head) row of D values to fp8 codes and its scale (see the header). */
+static void quantize_row(const void* x, int64_t base, int32_t d, int32_t in_dtype, uint8_t* codes, float* scale) {
+    float amax = 0.0f;
+    for (int32_t i = 0; i < d; ++i) {
+        const float f = fabsf((float)load_elem(x, base + i, in_dtype));
+        if (f > amax) amax = f;
+    }
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int32_t i = 0; i < d; ++i) codes[i] = oracle_fp8_e4m3_encode((float)load_elem(x, base + i, in_dtype) / s);
+    *scale = s;
+}
+
+/*
+ * write_kv into quantized pools: token i's K and V rows ([N, Hkv, D], in_dtype) become fp8
+ * codes in row s of k_cache / v_cache ([num_slots, Hkv, D] bytes) and their scales in
+ * k_scale / v_scale ([num_slots, Hkv] float32), s = slot_mapping[i] or the last slot if it is
+ * negative.
+ */
+int oracle_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, uint8_t* k_cache,
+                        uint8_t* v_cache, float* k_scale, float* v_scale, int64_t num_tokens,
+                        int32_t num_kv_heads, int32_t head_dim, int64_t num_slots, int32_t in_dtype) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        const int64_t s = slot_mapping[i] >= 0 ? slot_mapping[i] : num_slots - 1;
+        if (s >= num_slots) return -1;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            const int64_t src = i * row + (int64_t)h * head_dim, dst = s * row + (int64_t)h * head_dim;
+            quantize_row(k, src, head_dim, in_dtype, k_cache + dst, k_scale + s * num_kv_heads + h);
+            quantize_row(v, src, head_dim, in_dtype, v_cache + dst, v_scale + s * num_kv_heads + h);
+        }
+    }
+    return 0;
+}
 
 /*
  * Block copies of "Engine v2: one core for every request": swap_out gathers a preempted
@@ -118,6 +196,19 @@ int oracle_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
     return 0;
 }
 
+/* gather_context over a quantized pool: each element is its code's value times the scale of
+ * its (slot, KV head) row (ReferenceBackend.dequantize). */
+static void gather_fp8(const uint8_t* cache, const float* scale, const int32_t* table_row, int32_t length,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, double* out) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    for (int32_t p = 0; p < length; ++p) {
+        const int64_t slot = (int64_t)table_row[p / block_size] * block_size + p % block_size;
+        for (int64_t e = 0; e < row; ++e)
+            out[(int64_t)p * row + e] = oracle_fp8_e4m3_decode(cache[slot * row + e]) *
+                                        (double)scale[slot * num_kv_heads + e / head_dim];
+    }
+}
+
 /*
  * gather_context: the first `length` token rows of a request, in logical order.  Position p
  * lives at slot table[p / block_size] * block_size + p % block_size.  out is [length, Hkv, D].
@@ -135,8 +226,9 @@ void oracle_gather_context(const void* cache, const int32_t* table_row, int32_t 
 /*
  * ReferenceBackend.forward ("Attention over the pool").
  *
- * q, out: [N, H, D] in dtype; caches: [num_slots, Hkv, D] in dtype; query_start_loc [R+1];
- * seq_lens [R]; block_table [R, stride].  scale multiplies every score.
+ * q, out: [N, H, D] in dtype; caches: [num_slots, Hkv, D] in kv_dtype (dtype, or fp8 codes
+ * with k_scale / v_scale [num_slots, Hkv]); query_start_loc [R+1]; seq_lens [R]; block_table
+ * [R, stride].  scale multiplies every score.  window > 0: sliding window (see above).
  * out_f64, if not NULL, receives the unrounded float64 result ([N, H, D]).
  * row_mask, if not NULL, selects the flattened rows to compute ([N] bytes, nonzero = compute);
  * rows not selected are left untouched in both outputs.
@@ -148,7 +240,9 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
                            double* out_f64, int32_t num_reqs, int64_t num_tokens,
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_table_stride, int64_t num_slots, int32_t dtype,
-                           const uint8_t* row_mask, int32_t window) {
+                           const uint8_t* row_mask, int32_t window, int32_t kv_dtype,
+                           const float* k_scale, const float* v_scale) {
+    if (kv_dtype != dtype && (kv_dtype != ORACLE_FP8 || !k_scale || !v_scale)) return -1;
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0) return -1;
     if (query_start_loc[0] != 0 || query_start_loc[num_reqs] != num_tokens) return -1;
     for (int32_t r = 0; r < num_reqs; ++r) {
@@ -189,8 +283,13 @@ int oracle_paged_attention(const void* q, const void* k_cache, const void* v_cac
         double* ctx_k = (double*)malloc(sizeof(double) * (size_t)length * (size_t)kvrow);
         double* ctx_v = (double*)malloc(sizeof(double) * (size_t)length * (size_t)kvrow);
         if (!ctx_k || !ctx_v) { free(ctx_k); free(ctx_v); return -2; }
-        oracle_gather_context(k_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_k);
-        oracle_gather_context(v_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_v);
+        if (kv_dtype == ORACLE_FP8) {
+            gather_fp8((const uint8_t*)k_cache, k_scale, table_row, length, block_size, num_kv_heads, head_dim, ctx_k);
+            gather_fp8((const uint8_t*)v_cache, v_scale, table_row, length, block_size, num_kv_heads, head_dim, ctx_v);
+        } else {
+            oracle_gather_context(k_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_k);
+            oracle_gather_context(v_cache, table_row, length, block_size, num_kv_heads, head_dim, dtype, ctx_v);
+        }
 
         int failed = 0;
         #pragma omp parallel for collapse(2) schedule(dynamic, 1)

@@ -448,6 +448,97 @@ def check_copy_on_write(orc):
     assert _rel_err(after[1:2], sc.dense(1)) < 1e-6 and not np.array_equal(after[1], before[1])
 
 
+# ------------------------------------------------------------------------------------------
+# fp8 E4M3 pools with per-(slot, KV head) scales (ReferenceBackend.dequantize)
+# ------------------------------------------------------------------------------------------
+
+def _torch_fp8_decode(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_fp8_codec_vs_torch(orc):
+    """Every code decodes as torch's float8_e4m3fn does; float32 values round to the code
+    torch picks (nearest, ties to even) up to the overflow midpoint 464, and saturate past it."""
+    codes = np.arange(256)
+    want = _torch_fp8_decode(codes)
+    got = np.array([orc.fp8_e4m3_decode(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    rng = np.random.default_rng(41)
+    finite = want[~np.isnan(want)]
+    grid = np.unique(np.abs(finite))
+    mids = (grid[:-1] + grid[1:]) / 2                                    # exact ties
+    vals = np.concatenate([rng.standard_normal(3000) * 30, rng.standard_normal(1000) * 2e-3, mids, -mids,
+                           np.nextafter(mids.astype(np.float32), np.float32(0)), grid, [463.99, -463.99, 0.0, -0.0]])
+    vals = vals.astype(np.float32)
+    vals = vals[np.abs(vals) < 464]
+    want_codes = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got_codes = np.array([orc.fp8_e4m3_encode(float(x)) for x in vals], np.uint8)
+    assert np.array_equal(got_codes, want_codes), vals[got_codes != want_codes][:5]
+    for big in (464.0, 1e6, 3e38):
+        assert orc.fp8_e4m3_encode(big) == 0x7E and orc.fp8_e4m3_encode(-big) == 0xFE
+
+
+def _fp8_case(orc, seed, n=23, hkv=3, d=40, nb=9, bs=4):
+    rng = np.random.default_rng(seed)
+    k = (rng.standard_normal((n, hkv, d)) * rng.choice([1e-3, 1.0, 50.0], size=(n, hkv, 1))).astype(np.float32)
+    v = (rng.standard_normal((n, hkv, d)) * 3).astype(np.float32)
+    k[4, 1] = 0.0                                                        # an all-zero row: scale 1
+    kc = np.zeros((nb + 1, bs, hkv, d), np.uint8)
+    vc = kc.copy()
+    ks = np.zeros((nb + 1, bs, hkv), np.float32)
+    vs = ks.copy()
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    orc.kv_write_fp8(k, v, slots, kc, vc, ks, vs, "f32")
+    return k, v, slots, kc, vc, ks, vs
+
+
+def check_fp8_write_quantizes_each_row(orc):
+    """Each row's largest magnitude maps to code +-448 with scale max|x| / 448, and every
+    element dequantizes to within half an fp8 step (at its magnitude) of its value."""
+    k, v, slots, kc, vc, ks, vs = _fp8_case(orc, 42)
+    hkv, d = k.shape[1], k.shape[2]
+    for x, cache, sc in ((k, kc, ks), (v, vc, vs)):
+        codes = cache.reshape(-1, hkv, d)[slots]
+        scale = sc.reshape(-1, hkv)[slots].astype(np.float64)
+        deq = _torch_fp8_decode(codes) * scale[..., None]
+        amax = np.abs(x).max(axis=2)
+        nz = amax > 0
+        assert np.allclose(scale[nz], (amax[nz].astype(np.float32) / np.float32(448)).astype(np.float64), rtol=0)
+        assert np.all(scale[~nz] == 1.0) and np.all(codes[~nz] == 0)
+        assert np.all(np.abs(_torch_fp8_decode(codes)).max(axis=2)[nz] == 448.0)
+        y = np.abs(x / np.where(nz, scale, 1.0)[..., None])
+        step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+        assert np.all(np.abs(deq - x) <= 0.5 * step * scale[..., None] * (1 + 1e-6) + 1e-30)
+
+
+def check_fp8_attention_dequantizes(orc):
+    """Attention over fp8 pools equals dense attention over the dequantized rows (codes
+    decoded by torch, times their own (slot, KV head) scale)."""
+    sc = Scenario([(20, 3), (0, 6), (37, 1)], 6, 3, 40, 4, seed=43)
+    qsl, lens, table = sc.meta()
+    q = np.concatenate(sc.q, axis=0)
+    n_slots = (sc.num_blocks + 1) * sc.bs
+    kc = np.zeros((sc.num_blocks + 1, sc.bs, sc.Hkv, sc.D), np.uint8)
+    vc = kc.copy()
+    ks = np.zeros((sc.num_blocks + 1, sc.bs, sc.Hkv), np.float32)
+    vs = ks.copy()
+    for r, (c, t) in enumerate(sc.specs):
+        slots = np.array([workloads.slot_of(sc.tables[r], p, sc.bs) for p in range(c + t)], np.int64)
+        orc.kv_write_fp8(np.ascontiguousarray(sc.ctx_k[r]), np.ascontiguousarray(sc.ctx_v[r]), slots, kc, vc, ks, vs,
+                         "f32")
+    _, got = orc.paged_attention(q, kc, vc, qsl, lens, table, 1.0 / math.sqrt(sc.D), "f32", want_f64=True,
+                                 k_scale=ks, v_scale=vs)
+    row = 0
+    for r, (c, t) in enumerate(sc.specs):
+        slots = np.array([workloads.slot_of(sc.tables[r], p, sc.bs) for p in range(c + t)], np.int64)
+        dk = _torch_fp8_decode(kc.reshape(n_slots, sc.Hkv, sc.D)[slots]) * ks.reshape(n_slots, sc.Hkv)[slots][..., None]
+        dv = _torch_fp8_decode(vc.reshape(n_slots, sc.Hkv, sc.D)[slots]) * vs.reshape(n_slots, sc.Hkv)[slots][..., None]
+        want = dense_fold_attention(as_f64(sc.q[r], "f32"), dk, dv, 1.0 / math.sqrt(sc.D), c)
+        assert _rel_err(got[row:row + t], want) < 1e-12, r
+        row += t
+
+
 def check_padding_rows_zero(orc):
     """Padding rows (seq_len 0, one query row, slot -1) produce zeros, not 0/0."""
     b = workloads.small_batch([(5, 2), (0, 3)], pad_to=5, seed=9)
@@ -584,5 +675,6 @@ ALL_CHECKS = [
     check_padding_rows_zero, check_block_relabelling, check_aliasing, check_batch_composition,
     check_block_size_invariance, check_rejects_bad_metadata, check_window_dense, check_window_sdpa_bf16,
     check_window_one_is_own_v, check_window_zero_query_gives_window_mean, check_window_covering_context,
-    check_swap_roundtrip_preserves_attention, check_copy_on_write,
+    check_swap_roundtrip_preserves_attention, check_copy_on_write, check_fp8_codec_vs_torch,
+    check_fp8_write_quantizes_each_row, check_fp8_attention_dequantizes,
 ]

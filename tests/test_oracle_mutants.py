@@ -37,6 +37,11 @@ MUTANTS = [
      "unsigned char* to = (unsigned char*)dst + src_block[i] * block_bytes;"),
     ("copy_pairs_misaligned", "const unsigned char* from = (const unsigned char*)src + src_block[i] * block_bytes;",
      "const unsigned char* from = (const unsigned char*)src + src_block[i ? i - 1 : 0] * block_bytes;"),
+    ("fp8_exponent_bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 6)"),
+    ("fp8_round_half_up", "const double r = ldexp(rint(ldexp(a, -q)), q);", "const double r = ldexp(floor(ldexp(a, -q) + 0.5), q);"),
+    ("fp8_scale_constant", "amax / 448.0f", "amax / 240.0f"),
+    ("fp8_scale_of_wrong_head", "(double)scale[slot * num_kv_heads + e / head_dim]", "(double)scale[slot * num_kv_heads]"),
+    ("fp8_subnormals_flushed", "if (Er < -6) return sign | (uint8_t)ldexp(r, 9);", "if (Er < -6) return sign;"),
 ]
 
 
