@@ -44,6 +44,7 @@ extern "C" {
 
 #define PA_DTYPE_F32 0
 #define PA_DTYPE_BF16 1
+#define PA_DTYPE_FP8_E4M3 2     /* KV pools only: OCP E4M3 codes with a float32 scale per (slot, KV head) */
 
 /*
  * paged_kv_write: write_kv of "Attention over the pool".
@@ -65,6 +66,25 @@ extern "C" {
 int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
                    void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                    int64_t num_slots, int32_t in_dtype, int32_t cache_dtype, hipStream_t stream);
+
+/*
+ * paged_kv_write_fp8: write_kv into quantized pools.  ReferenceBackend.dequantize of
+ * "Attention over the pool" reads a quantized pool as its codes' values times the scale kept
+ * beside it for each (slot, KV head); this is the write that matches it.
+ *
+ * For every token i and KV head h, the row x = k[i, h, :] (and likewise v) becomes
+ *     scale = max_d |x_d| / 448   (1 if the row is all zero; float32 division)
+ *     code_d = the fp8 E4M3 value nearest to x_d / scale (float32 division, ties to even;
+ *              E4M3 here is the OCP "FN" format: largest finite 448, no infinities)
+ * stored at row s of k_cache / v_cache ([num_slots, num_kv_heads, head_dim] bytes) and at
+ * k_scale / v_scale[s * num_kv_heads + h] ([num_slots, num_kv_heads] float32), with
+ * s = slot_mapping[i], or num_slots - 1 if it is negative.  k, v: [num_tokens,
+ * num_kv_heads, head_dim] in in_dtype (PA_DTYPE_F32 or PA_DTYPE_BF16); head_dim <= 256.
+ * Preconditions and errors as for paged_kv_write; values must be finite.
+ */
+int paged_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                       float* k_scale, float* v_scale, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_slots, int32_t in_dtype, hipStream_t stream);
 
 /*
  * paged_copy_blocks: the block copies of preemption and prefix sharing, swap_out /
@@ -167,14 +187,27 @@ int paged_attention_varlen(const void* q, const void* k_cache, const void* v_cac
  *                      (decode and verification batches); seq_lens above M are a
  *                      precondition violation (not checked).  No call made by the library
  *                      inside such a capture allocates or uses hipMemset.
+ *   kv_cache_dtype     PA_DTYPE_FP8_E4M3: k_cache / v_cache hold fp8 codes (one byte per
+ *                      element) written by paged_kv_write_fp8, and every key and value is
+ *                      its code's value times its (slot, KV head) scale from k_scale /
+ *                      v_scale (ReferenceBackend.dequantize).  Needs dtype PA_DTYPE_BF16,
+ *                      block_size 16 and head_dim 64 or 128; every request then takes the
+ *                      small-tile kernel (K codes and V codes convert exactly to bf16; each
+ *                      score is multiplied by its key's K scale and each probability by its
+ *                      key's V scale).  Else PA_ERR_DTYPE.
  */
 typedef struct pa_attention_options {
   int32_t sliding_window;
   int32_t graph_max_seq_len;
-  int32_t reserved[6];
+  int32_t kv_cache_dtype;      /* 0: the pools hold `dtype`; PA_DTYPE_FP8_E4M3: fp8 codes, see below */
+  int32_t reserved0;
+  const float* k_scale;        /* fp8 pools: [num_slots, num_kv_heads] float32 scales of K and V */
+  const float* v_scale;
+  int64_t reserved[4];
 } pa_attention_options;
 
-/* paged_attention_workspace_bytes with options (the workspace depends on the window). */
+/* paged_attention_workspace_bytes with options (the workspace depends on the window, the
+ * sizing and the pool dtype; the scale pointers are not read here and may be NULL). */
 size_t paged_attention_workspace_bytes_ex(int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                           const int32_t* query_start_loc_host,

@@ -23,9 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+PA_DTYPE_FP8_E4M3 = 2
 ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
           -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
-EXPORTS = ["paged_kv_write", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
+EXPORTS = ["paged_kv_write", "paged_kv_write_fp8", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
            "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
            "paged_attn_set_timing", "paged_attn_timing_report"]
@@ -37,7 +38,8 @@ _lib = None
 class AttentionOptions(ctypes.Structure):
     """pa_attention_options of the C ABI."""
     _fields_ = [("sliding_window", ctypes.c_int32), ("graph_max_seq_len", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("kv_cache_dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("reserved", ctypes.c_int64 * 4)]
 
 
 class PagedAttnError(RuntimeError):
@@ -57,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, P]
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
+    lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I64, I32, P]
     lib.paged_copy_blocks.restype = ctypes.c_int
     lib.paged_copy_blocks.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
     lib.paged_attention_workspace_bytes.restype = SZ
@@ -152,11 +156,38 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                               PA_DTYPE[k.dtype], PA_DTYPE[k_cache.dtype], _stream(stream)))
 
 
-def _options(sliding_window: int, graph_max_seq_len: int = 0):
+def _options(sliding_window: int, graph_max_seq_len: int = 0, k_scale=None, v_scale=None, fp8: bool = False):
     opts = AttentionOptions()
     opts.sliding_window = int(sliding_window)
     opts.graph_max_seq_len = int(graph_max_seq_len)
+    if k_scale is not None or fp8:
+        opts.kv_cache_dtype = PA_DTYPE_FP8_E4M3
+    if k_scale is not None:
+        opts.k_scale = k_scale.data_ptr()
+        opts.v_scale = v_scale.data_ptr()
     return ctypes.byref(opts), opts
+
+
+def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, stream=None) -> None:
+    """Quantize k, v [N, Hkv, D] (f32 or bf16) into fp8 E4M3 pools k_cache / v_cache
+    ([NB+1, bs, Hkv, D] uint8) and their per-(slot, KV head) scales k_scale / v_scale
+    ([NB+1, bs, Hkv] float32) at slot_mapping (int64; negative: the scratch slot)."""
+    lib = load_library()
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    n, hkv, d = k.shape
+    if v.shape != k.shape or k_cache.shape != v_cache.shape or tuple(k_cache.shape[2:]) != (hkv, d):
+        raise ValueError("shape mismatch between k, v and the caches")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 pools are uint8 tensors of codes")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError(f"{name} must be float32 [NB+1, bs, Hkv]")
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    _check(lib.paged_kv_write_fp8(_dptr(k, "k"), _dptr(v, "v"), _dptr(slot_mapping, "slot_mapping"),
+                                  _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"), _dptr(k_scale, "k_scale"),
+                                  _dptr(v_scale, "v_scale"), n, hkv, d, num_slots, PA_DTYPE[k.dtype], _stream(stream)))
 
 
 def paged_copy_blocks(src: torch.Tensor, dst: torch.Tensor, src_block: torch.Tensor, dst_block: torch.Tensor,
@@ -184,11 +215,12 @@ def paged_copy_blocks(src: torch.Tensor, dst: torch.Tensor, src_block: torch.Ten
 
 def paged_attention_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                                     query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
-                                    dtype: torch.dtype, sliding_window: int = 0, graph_max_seq_len: int = 0) -> int:
+                                    dtype: torch.dtype, sliding_window: int = 0, graph_max_seq_len: int = 0,
+                                    kv_fp8: bool = False) -> int:
     lib = load_library()
     r = len(query_start_loc_host) - 1
     n = int(query_start_loc_host[-1]) if r > 0 else 0
-    ref, _keep = _options(sliding_window, graph_max_seq_len)
+    ref, _keep = _options(sliding_window, graph_max_seq_len, fp8=kv_fp8)
     lens = _host_i32(seq_lens_host) if seq_lens_host is not None else None
     return int(lib.paged_attention_workspace_bytes_ex(r, n, num_heads, num_kv_heads, head_dim, block_size,
                                                       _host_i32(query_start_loc_host), lens, PA_DTYPE[dtype], ref))
@@ -200,16 +232,29 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            query_start_loc_host: Sequence[int], seq_lens_host: Sequence[int],
                            max_query_len: int = 0, max_seq_len: int = 0,
                            workspace: Optional[torch.Tensor] = None, stream=None,
-                           sliding_window: int = 0, graph_max_seq_len: int = 0) -> torch.Tensor:
+                           sliding_window: int = 0, graph_max_seq_len: int = 0,
+                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None
+                           ) -> torch.Tensor:
     """Causal attention of the flattened batch over the pool; returns out [N, H, D].
     sliding_window > 0 limits the row at position p to keys p - sliding_window + 1 .. p.
     graph_max_seq_len > 0 sizes the launches for any device seq_lens up to it (for a call
-    captured in a graph and replayed as the contexts grow); seq_lens_host may be None."""
+    captured in a graph and replayed as the contexts grow); seq_lens_host may be None.
+    With k_scale / v_scale ([NB+1, bs, Hkv] float32) the caches are fp8 E4M3 pools (uint8
+    codes written by paged_kv_write_fp8) and q / out are bf16."""
     lib = load_library()
     n, h, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[1] != block_size or k_cache.shape[3] != d:
         raise ValueError("cache shape must be [num_blocks + 1, block_size, Hkv, D]")
-    if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
+    fp8 = k_scale is not None
+    if fp8:
+        if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8 or v_scale is None:
+            raise ValueError("fp8 pools: uint8 caches with k_scale and v_scale")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]) or not t.is_cuda:
+                raise ValueError(f"{name} must be a float32 device tensor [NB+1, bs, Hkv]")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    elif q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
         raise ValueError("q and the caches must share a dtype")
     for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens), ("block_table", block_table)):
         if t.dtype != torch.int32:
@@ -220,7 +265,7 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     r = len(query_start_loc_host) - 1
     qh = _host_i32(query_start_loc_host)
     sh = _host_i32(seq_lens_host) if seq_lens_host is not None else None
-    ref, _keep = _options(sliding_window, graph_max_seq_len)
+    ref, _keep = _options(sliding_window, graph_max_seq_len, k_scale, v_scale)
     need = lib.paged_attention_workspace_bytes_ex(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype], ref)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)

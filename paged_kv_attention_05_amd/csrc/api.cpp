@@ -63,23 +63,36 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Options of the _ex entry points (NULL: defaults).  Reserved fields must be zero.
-int read_options(const pa_attention_options* o, int32_t* window, int32_t* graph_max) {
-  *window = 0;
-  *graph_max = 0;
+struct Options {
+  int32_t window = 0, graph_max = 0;
+  bool fp8 = false;
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
+};
+int read_options(const pa_attention_options* o, Options* out, bool need_scales) {
+  *out = Options{};
   if (!o) return PA_OK;
-  for (int32_t x : o->reserved)
+  for (int64_t x : o->reserved)
     if (x != 0) return fail(PA_ERR_SHAPE, "pa_attention_options.reserved must be zero");
+  if (o->reserved0 != 0) return fail(PA_ERR_SHAPE, "pa_attention_options.reserved0 must be zero");
+  if (o->kv_cache_dtype != 0 && o->kv_cache_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "kv_cache_dtype must be 0 or PA_DTYPE_FP8_E4M3");
+  out->fp8 = o->kv_cache_dtype == PA_DTYPE_FP8_E4M3;
+  out->k_scale = o->k_scale;
+  out->v_scale = o->v_scale;
+  if (need_scales && out->fp8 && (!o->k_scale || !o->v_scale))
+    return fail(PA_ERR_NULL, "fp8 pools need k_scale and v_scale");
   if (o->sliding_window < 0) return fail(PA_ERR_SHAPE, "sliding_window must be >= 0");
   if (o->graph_max_seq_len < 0) return fail(PA_ERR_SHAPE, "graph_max_seq_len must be >= 0");
-  *window = o->sliding_window;
-  *graph_max = o->graph_max_seq_len;
+  out->window = o->sliding_window;
+  out->graph_max = o->graph_max_seq_len;
   return PA_OK;
 }
 
 // Validates the host metadata and builds the plan.  Returns PA_OK or an error code.
 int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t bs, int32_t stride,
               const int32_t* qsl, const int32_t* lens_host, int32_t dtype, int32_t window, int32_t graph_max,
-              pa::Plan* out) {
+              bool fp8, pa::Plan* out) {
   // with graph_max the launches are sized as if every seq_len were graph_max
   std::vector<int32_t> capacity;
   const int32_t* lens = lens_host;
@@ -115,9 +128,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
   p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
   const bool auto_path = g_path == 0;
-  p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
+  p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && !fp8 && pa::prefill_mfma_supported(D, bs, p.g))
                     ? pa::prefill_tile_tokens(p.g) : 0;
   p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs)) ? 1 : 0;
+  if (fp8 && p.decode_kind != 1)
+    return fail(PA_ERR_DTYPE, "fp8 pools need dtype bf16, block_size 16, head_dim 64 or 128 and the automatic path");
 
   // pass 1: validate and measure the small-tile work to size the key splits
   double small_keys = 0;
@@ -232,6 +247,37 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, vo
   return PA_OK;
 }
 
+int paged_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                       float* k_scale, float* v_scale, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_slots, int32_t in_dtype, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || head_dim > 256)
+    return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0 and head_dim in 1 .. 256");
+  if (num_slots < 1) return fail(PA_ERR_SHAPE, "num_slots must be >= 1 (the scratch slot)");
+  if (in_dtype != PA_DTYPE_F32 && in_dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "in_dtype must be f32 or bf16");
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return fail(PA_ERR_NULL, "null pointer argument");
+  if (g_debug_checks) {
+    std::vector<int64_t> s((size_t)num_tokens);
+    if (hipMemcpy(s.data(), slot_mapping, sizeof(int64_t) * s.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "debug check: copy of slot_mapping failed");
+    std::unordered_set<int64_t> seen;
+    for (size_t i = 0; i < s.size(); ++i) {
+      if (s[i] >= num_slots) return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] out of range");
+      if (s[i] >= 0 && !seen.insert(s[i]).second)
+        return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] repeats a slot");
+    }
+  }
+  const hipError_t e = timed(PA_KIND_KV_WRITE, stream, [&] {
+    return pa::launch_kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens, num_kv_heads,
+                                   head_dim, num_slots, in_dtype, stream);
+  });
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("kv write launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 int paged_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
                       int64_t num_pairs, int64_t block_bytes, int64_t num_src_blocks, int64_t num_dst_blocks,
                       hipStream_t stream) {
@@ -278,11 +324,11 @@ size_t paged_attention_workspace_bytes_ex(int32_t num_reqs, int64_t num_tokens, 
                                           int32_t dtype, const pa_attention_options* options) {
   pa::Plan p;
   const std::string keep = g_last_error;
-  int32_t window = 0, graph_max = 0;
-  int rc = read_options(options, &window, &graph_max);
+  Options opt;
+  int rc = read_options(options, &opt, false);
   if (rc == PA_OK)
     rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, INT32_MAX,
-                   query_start_loc_host, seq_lens_host, dtype, window, graph_max, &p);
+                   query_start_loc_host, seq_lens_host, dtype, opt.window, opt.graph_max, opt.fp8, &p);
   g_last_error = keep;
   return rc == PA_OK ? p.total_bytes : 0;
 }
@@ -315,12 +361,13 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   (void)max_query_len;
   (void)max_seq_len;
   if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
-  int32_t window = 0, graph_max = 0;
-  int rc = read_options(options, &window, &graph_max);
+  Options opt;
+  int rc = read_options(options, &opt, true);
   if (rc != PA_OK) return rc;
+  const int32_t graph_max = opt.graph_max;
   pa::Plan p;
   rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                 query_start_loc_host, seq_lens_host, dtype, window, graph_max, &p);
+                 query_start_loc_host, seq_lens_host, dtype, opt.window, opt.graph_max, opt.fp8, &p);
   if (rc != PA_OK) return rc;
   if (num_reqs == 0) return PA_OK;
   if (!query_start_loc || !seq_lens || !block_table || !workspace) return fail(PA_ERR_NULL, "null pointer argument");
@@ -354,6 +401,8 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   a.split_keys = p.split_keys;
   a.window = p.window;
   a.totals = (const int32_t*)((const char*)workspace + p.off_req + sizeof(pa::ReqOffsets) * (size_t)num_reqs);
+  a.k_scale = opt.fp8 ? opt.k_scale : nullptr;
+  a.v_scale = opt.fp8 ? opt.v_scale : nullptr;
   a.scale_log2e = scale * 1.4426950408889634f;
 
   hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });

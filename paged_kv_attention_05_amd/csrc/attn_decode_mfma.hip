@@ -36,6 +36,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBlk = 16;                      // keys per block (block_size)
@@ -69,7 +71,19 @@ __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wav
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-template <int D>
+// four fp8 E4M3 codes (one dword) to four bf16 values, exactly (4 significant bits fit in 8)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  const bf16x4 r = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)hi[0], (__bf16)hi[1]};
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// F8: the pools hold fp8 E4M3 codes with a float32 scale per (slot, KV head) (a.k_scale,
+// a.v_scale).  K codes convert exactly to bf16 for the QK^T product and each score is then
+// multiplied by its key's scale; V codes convert exactly to bf16 into the wave's LDS buffer,
+// and each probability is multiplied by its key's V scale before the PV product (the row sum
+// takes the probabilities alone), so sum_j p_j (s_j v8_j) = sum_j (p_j s_j) v8_j.
+template <int D, bool F8>
 __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
                                                        Partials part) {
   using C = DecodeCfg<D>;
@@ -119,6 +133,8 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const __bf16* kc = (const __bf16*)a.k_cache + (int64_t)hkv * D;
   const __bf16* vc = (const __bf16*)a.v_cache + (int64_t)hkv * D;
+  const uint8_t* kc8 = (const uint8_t*)a.k_cache + (int64_t)hkv * D;   // F8: bytes
+  const uint8_t* vc8 = (const uint8_t*)a.v_cache + (int64_t)hkv * D;
 
   // Q^T as the B operand: column n, dims 32*kk + 8*G .. +7; a negative scale becomes -q
   const float sl = fmaxf(fabsf(a.scale_log2e), 1e-30f);
@@ -164,11 +180,47 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     }
   };
 
-  auto compute = [&](int32_t lb, const bf16x8* kcur, const unsigned char* vb) {
+  // F8 loads: K codes of key n (8 bytes per k-chunk), V codes of row lane/4 (D/4 bytes), and
+  // the scales of the lane's four S^T keys 4G .. 4G+3
+  constexpr int VB = D / 4;                                   // V bytes per lane and block
+  struct F8Block { u32x2 k[C::KC]; u32x4 v[VB / 16]; float ks[4], vs[4]; };
+  auto load_f8 = [&](int32_t lb, F8Block& f) {
+    const uint8_t* kp = kc8 + slot_of_key(lb * kBlk + n) * row_elems + 8 * G;
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) f.k[kk] = *(const u32x2*)(kp + 32 * kk);
+    const uint8_t* vp = vc8 + slot_of_key(lb * kBlk + (lane >> 2)) * row_elems + VB * (lane & 3);
+#pragma unroll
+    for (int x = 0; x < VB / 16; ++x) f.v[x] = *(const u32x4*)(vp + 16 * x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t sidx = slot_of_key(lb * kBlk + 4 * G + i) * a.Hkv + hkv;
+      f.ks[i] = a.k_scale[sidx];
+      f.vs[i] = a.v_scale[sidx];
+    }
+  };
+  // V codes of one block to bf16 in the wave's LDS buffer, same swizzled rows as the bf16 path
+  auto stage_v = [&](const F8Block& f, unsigned char* dst) {
+    const int r = lane >> 2;
+#pragma unroll
+    for (int x = 0; x < VB / 16; ++x) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int chunk = (VB * (lane & 3) + 16 * x + 8 * hf) / 8;   // 8 elements per chunk
+        const u32x2 a0 = fp8x4_to_bf16x4(f.v[x][2 * hf]), a1 = fp8x4_to_bf16x4(f.v[x][2 * hf + 1]);
+        *(u32x4*)(dst + r * C::ROW + 16 * (chunk ^ vswz<D>(r))) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      }
+    }
+  };
+
+  auto compute = [&](int32_t lb, const bf16x8* kcur, const unsigned char* vb, const float* ks, const float* vs) {
     // S^T = K Q^T
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kk], qf[kk], s, 0, 0, 0);
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] *= ks[i];
+    }
     // masked scores, running max (base 2)
     const int32_t key0 = lb * kBlk + 4 * G;
     float sv[4];
@@ -186,6 +238,10 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl, -m_use));
     lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] *= vs[i];
+    }
     bf16x4 phi, plo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -207,6 +263,28 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   // blocks blk0, blk0 + 4, ... of this wave, two at a time: K ping-pongs between two register
   // sets, V between two LDS buffers; the next block's loads are in flight during each compute
   bf16x8 kA[C::KC], kB[C::KC];
+  if constexpr (F8) {
+    // codes ping-pong between two register sets (plain loads: the compiler waits for them)
+    F8Block fA, fB;
+    auto run = [&](int32_t lb, const F8Block& f, unsigned char* vb) {
+      stage_v(f, vb);
+      bf16x8 kr[C::KC];
+#pragma unroll
+      for (int kk = 0; kk < C::KC; ++kk) {
+        const u32x2 a0 = fp8x4_to_bf16x4(f.k[kk][0]), a1 = fp8x4_to_bf16x4(f.k[kk][1]);
+        kr[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+      }
+      compute(lb, kr, vb, f.ks, f.vs);
+    };
+    if (blk0 < nblk_end) load_f8(blk0, fA);
+    for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
+      if (lb + 4 < nblk_end) load_f8(lb + 4, fB);
+      run(lb, fA, vbuf0);
+      if (lb + 4 >= nblk_end) break;
+      if (lb + 8 < nblk_end) load_f8(lb + 8, fA);
+      run(lb + 4, fB, vbuf0 + C::VBUF);
+    }
+  } else {
   if (blk0 < nblk_end) {
     load_k(blk0, kA);
     load_v(blk0, vbuf0);
@@ -220,7 +298,7 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    compute(lb, kA, vbuf0);
+    compute(lb, kA, vbuf0, nullptr, nullptr);
     if (!has1) break;
     const bool has2 = lb + 8 < nblk_end;
     if (has2) {
@@ -230,7 +308,8 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    compute(lb + 4, kB, vbuf0 + C::VBUF);
+    compute(lb + 4, kB, vbuf0 + C::VBUF, nullptr, nullptr);
+  }
   }
 
   // combine the four waves: per column max, sum and output
@@ -301,8 +380,11 @@ hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStre
   const SmallItem* items = (const SmallItem*)(w + p.off_small);
   Partials part{(float*)(w + p.off_pm), (float*)(w + p.off_pl), (float*)(w + p.off_pacc)};
   const dim3 grid((unsigned)p.n_small, (unsigned)p.Hkv);
-  if (p.D == 128) hipLaunchKernelGGL(small_tile_mfma<128>, grid, dim3(256), 0, s, a, items, part);
-  else if (p.D == 64) hipLaunchKernelGGL(small_tile_mfma<64>, grid, dim3(256), 0, s, a, items, part);
+  const bool f8 = a.k_scale != nullptr;
+  if (p.D == 128 && !f8) hipLaunchKernelGGL((small_tile_mfma<128, false>), grid, dim3(256), 0, s, a, items, part);
+  else if (p.D == 64 && !f8) hipLaunchKernelGGL((small_tile_mfma<64, false>), grid, dim3(256), 0, s, a, items, part);
+  else if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, true>), grid, dim3(256), 0, s, a, items, part);
+  else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, true>), grid, dim3(256), 0, s, a, items, part);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -126,6 +126,9 @@ struct AttnArgs {
   // Grids are sized on the host; a workgroup past the device count exits (the counts agree
   // except when a captured graph replays with shorter contexts than it was sized for).
   const int32_t* totals;
+  // fp8 pools: float32 scales [num_slots, Hkv] of K and V (null: the pools hold q's dtype)
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct Partials {
@@ -139,6 +142,9 @@ hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, v
                            int64_t n, int32_t row_elems, int64_t num_slots, int32_t in_dtype,
                            int32_t cache_dtype, hipStream_t s);
 hipError_t launch_plan(const Plan& p, const int32_t* qsl, const int32_t* seq_lens, void* ws, hipStream_t s);
+hipError_t launch_kv_write_fp8(const void* k, const void* v, const int64_t* slots, void* kc, void* vc, float* ks,
+                               float* vs, int64_t n, int32_t hkv, int32_t d, int64_t num_slots, int32_t in_dtype,
+                               hipStream_t s);
 hipError_t launch_copy_blocks(const void* src, void* dst, const int64_t* src_block, const int64_t* dst_block,
                               int64_t num_pairs, int64_t block_bytes, hipStream_t s);
 hipError_t launch_small_valu(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);

@@ -141,6 +141,115 @@ def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     H.check_batch(b, label=name)
 
 
+# ------------------------------------------------------------------------- fp8 pools
+def _fp8_pools(b):
+    """The batch's context pool quantized slot by slot with the oracle's write: codes and scales."""
+    import oracle
+    from tests._util import to_np
+    shape = tuple(b.k_cache.shape)
+    kc = np.zeros(shape, np.uint8)
+    vc = np.zeros(shape, np.uint8)
+    ks = np.zeros(shape[:3], np.float32)
+    vs = np.zeros(shape[:3], np.float32)
+    flat = lambda t: np.ascontiguousarray(to_np(t).reshape(-1, shape[2], shape[3]))
+    oracle.kv_write_fp8(flat(b.k_cache), flat(b.v_cache), np.arange(shape[0] * shape[1], dtype=np.int64),
+                        kc, vc, ks, vs, b.dtype)
+    return kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_kv_write_fp8_parity(in_dtype):
+    """Codes and scales bit for bit as the oracle's write (both divide in float32)."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(71)
+    n, hkv, d, nb, bs = 300, 8, 128, 40, 16
+    k = torch.randn((n, hkv, d), generator=gen) * torch.tensor([1e-4, 1.0, 30.0, 1e3])[torch.arange(n) % 4][:, None, None]
+    v = torch.randn((n, hkv, d), generator=gen) * 2
+    k[5, 3] = 0.0
+    k, v = k.to(workloads.TORCH_DTYPES[in_dtype]), v.to(workloads.TORCH_DTYPES[in_dtype])
+    slots = torch.randperm(nb * bs, generator=gen)[:n].to(torch.int64)
+    slots[[7, 100]] = -1
+    kc = torch.zeros((nb + 1, bs, hkv, d), dtype=torch.uint8)
+    vc, ks, vs = kc.clone(), torch.zeros((nb + 1, bs, hkv)), torch.zeros((nb + 1, bs, hkv))
+    okc, ovc, oks, ovs = kc.numpy().copy(), vc.numpy().copy(), ks.numpy().copy(), vs.numpy().copy()
+    oracle.kv_write_fp8(to_np(k), to_np(v), slots.numpy(), okc, ovc, oks, ovs, in_dtype)
+    g = [t.to(dev) for t in (kc, vc, ks, vs)]
+    pk.paged_kv_write_fp8(k.to(dev), v.to(dev), slots.to(dev), *g)
+    torch.cuda.synchronize()
+    live = np.ones((nb + 1) * bs, bool)
+    live[-1] = False                                   # padding rows race for the scratch slot
+    for got, want in zip(g, (okc, ovc, oks, ovs)):
+        got = got.cpu().numpy().reshape((nb + 1) * bs, -1)[live]
+        assert np.array_equal(got.view(np.uint8), want.reshape((nb + 1) * bs, -1)[live].view(np.uint8))
+
+
+FP8 = [
+    # (name, specs, H, Hkv, D, window)
+    ("decodes", [(1000, 1), (15, 1), (300, 1), (5000, 1), (0, 1)], 32, 8, 128, 0),
+    ("chunks_on_small_tiles", [(700, 150), (90, 1), (0, 300)], 32, 8, 128, 0),
+    ("spec_rows_d64", [(100, 2), (57, 3), (300, 4), (16, 5)], 8, 2, 64, 0),
+    ("window", [(3000, 1), (200, 40), (9, 1)], 32, 8, 128, 100),
+]
+
+
+@pytest.mark.parametrize("name,specs,h,hkv,d,window", FP8, ids=[f[0] for f in FP8])
+def test_fp8_attention_parity(name, specs, h, hkv, d, window):
+    """The step on fp8 pools: the write of the new tokens bit-exact, attention within the
+    bf16 bound of the oracle's attention over the dequantized pools."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    b = workloads.small_batch(specs, dtype="bf16", num_heads=h, num_kv_heads=hkv, head_dim=d,
+                              seed=zlib.crc32(name.encode()) % 1000)
+    kc, vc, ks, vs = _fp8_pools(b)
+    g = [torch.from_numpy(x.copy()).to(dev) for x in (kc, vc, ks, vs)]
+    pk.paged_kv_write_fp8(b.k.to(dev), b.v.to(dev), b.slot_mapping.to(dev), *g)
+    out = pk.paged_attention_varlen(b.q.to(dev), g[0], g[1], b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                    b.block_table.to(dev), b.block_size, b.scale,
+                                    query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host,
+                                    sliding_window=window, k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    oracle.kv_write_fp8(to_np(b.k), to_np(b.v), b.slot_mapping.numpy(), kc, vc, ks, vs, "bf16")
+    n = kc.shape[0] * kc.shape[1]
+    for got, want in zip(g, (kc, vc, ks, vs)):
+        assert np.array_equal(got.cpu().numpy().reshape(n, -1)[:-1].view(np.uint8),
+                              want.reshape(n, -1)[:-1].view(np.uint8))
+    _, ref64 = oracle.paged_attention(to_np(b.q), kc, vc, b.query_start_loc.numpy(), b.seq_lens.numpy(),
+                                      b.block_table.numpy(), b.scale, "bf16", want_f64=True, window=window,
+                                      k_scale=ks, v_scale=vs)
+    err = attention_error(out.float().cpu().numpy(), ref64, "bf16")
+    H.log(f"[parity] fp8_{name}: error {err:.3g} x bound")
+    H.record({"case": f"fp8_{name}", "dtype": "bf16", "kv": "fp8_e4m3", "window": window, "error_x_bound": err})
+    assert err <= 1.0, err
+
+
+def test_fp8_decode_only_full_size():
+    """The 256-decode batch (seq_len 512..8192) on fp8 pools, every row."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    b = workloads.decode_only()
+    kc, vc, ks, vs = _fp8_pools(b)
+    g = [torch.from_numpy(x.copy()).to(dev) for x in (kc, vc, ks, vs)]
+    pk.paged_kv_write_fp8(b.k.to(dev), b.v.to(dev), b.slot_mapping.to(dev), *g)
+    out = pk.paged_attention_varlen(b.q.to(dev), g[0], g[1], b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                    b.block_table.to(dev), b.block_size, b.scale,
+                                    query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host,
+                                    k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    oracle.kv_write_fp8(to_np(b.k), to_np(b.v), b.slot_mapping.numpy(), kc, vc, ks, vs, "bf16")
+    _, ref64 = oracle.paged_attention(to_np(b.q), kc, vc, b.query_start_loc.numpy(), b.seq_lens.numpy(),
+                                      b.block_table.numpy(), b.scale, "bf16", want_f64=True, k_scale=ks, v_scale=vs)
+    err = attention_error(out.float().cpu().numpy(), ref64, "bf16")
+    H.record({"case": "fp8_decode_only", "dtype": "bf16", "kv": "fp8_e4m3", "error_x_bound": err})
+    assert err <= 1.0, err
+
+
 # ------------------------------------------------------------------------- block copies
 @pytest.mark.parametrize("dtype,shape", [("bf16", (41, 16, 8, 128)), ("f32", (23, 16, 4, 48)), ("bf16", (25, 1, 1, 8))],
                          ids=["bf16_d128", "f32_d48", "bf16_tiny_block"])
