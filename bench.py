@@ -76,6 +76,11 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="capture the step once in a HIP graph (launches sized for the batch's max seq_len) "
                          "and time graph replays; per-kernel times still come from eager steps")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="keep the pools as fp8 E4M3 codes with a float32 scale per (slot, KV head): the "
+                         "pool is quantized once before the steps, each step writes its tokens through the "
+                         "quantizing write and attends over the codes (bf16 batches; every request on the "
+                         "small tiles)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once: a plain copy "
                          "of known size whose HBM counters scale the kernels' counters")
@@ -109,31 +114,52 @@ def main() -> int:
 
     q, k, v = batch.q.to(dev), batch.k.to(dev), batch.v.to(dev)
     kc, vc = batch.k_cache.to(dev), batch.v_cache.to(dev)
+    ks = vs = None
+    if args.kv_fp8:
+        if batch.dtype != "bf16":
+            eprint("--kv-fp8 needs a bf16 workload")
+            return 2
+        # the whole pool through the quantizing write once (setup, not timed)
+        nslots = kc.shape[0] * kc.shape[1]
+        codes = [torch.empty(kc.shape, dtype=torch.uint8, device=dev) for _ in range(2)]
+        scales = [torch.empty(kc.shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+        pk.paged_kv_write_fp8(kc.view(nslots, *kc.shape[2:]), vc.view(nslots, *vc.shape[2:]),
+                              torch.arange(nslots, dtype=torch.int64, device=dev), *codes, *scales)
+        torch.cuda.synchronize()
+        kc, vc = codes
+        ks, vs = scales
+        del codes, scales
+        torch.cuda.empty_cache()
     qsl, lens = batch.query_start_loc.to(dev), batch.seq_lens.to(dev)
     table, slots = batch.block_table.to(dev), batch.slot_mapping.to(dev)
     out = torch.empty_like(q)
     ws_bytes = pk.paged_attention_workspace_bytes(batch.num_heads, batch.num_kv_heads, batch.head_dim,
                                                   batch.block_size, batch.query_start_loc_host,
-                                                  batch.seq_lens_host, q.dtype, sliding_window=args.window)
+                                                  batch.seq_lens_host, q.dtype, sliding_window=args.window,
+                                                  kv_fp8=args.kv_fp8)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     graph_max = batch.max_seq_len if args.graph else 0
     if args.graph:
         ws_bytes = pk.paged_attention_workspace_bytes(batch.num_heads, batch.num_kv_heads, batch.head_dim,
                                                       batch.block_size, batch.query_start_loc_host, None, q.dtype,
-                                                      sliding_window=args.window, graph_max_seq_len=graph_max)
+                                                      sliding_window=args.window, graph_max_seq_len=graph_max,
+                                                      kv_fp8=args.kv_fp8)
         if ws_bytes == 0:
             eprint("--graph needs every request to have at most 64 query columns (decode-like batches)")
             return 2
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
-        pk.paged_kv_write(k, v, slots, kc, vc)
+        if args.kv_fp8:
+            pk.paged_kv_write_fp8(k, v, slots, kc, vc, ks, vs)
+        else:
+            pk.paged_kv_write(k, v, slots, kc, vc)
         pk.paged_attention_varlen(q, kc, vc, qsl, lens, table, batch.block_size, batch.scale, out,
                                   query_start_loc_host=batch.query_start_loc_host,
                                   seq_lens_host=batch.seq_lens_host, max_query_len=batch.max_query_len,
                                   max_seq_len=batch.max_seq_len, workspace=ws, sliding_window=args.window,
-                                  graph_max_seq_len=graph_max)
+                                  graph_max_seq_len=graph_max, k_scale=ks, v_scale=vs)
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -187,16 +213,17 @@ def main() -> int:
     # algorithmic work, split the way the library routes requests
     g = batch.num_heads // batch.num_kv_heads
     prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim == 128 \
-        and 256 % g == 0
+        and 256 % g == 0 and not args.kv_fp8
     is_pf = [prefill_capable and r.new * g > PREFILL_MIN_COLS and r.seq_len > 0 for r in batch.requests]
     if kern["prefill"][1] == 0:          # the library routed every request to the small tiles
         is_pf = [False] * len(is_pf)
     pf_ids = [i for i, f in enumerate(is_pf) if f]
     dec_ids = [i for i, f in enumerate(is_pf) if not f]
-    w_all = attention_work(batch, window=args.window)
-    w_dec = attention_work(batch, dec_ids, window=args.window) if dec_ids else None
-    w_pf = attention_work(batch, pf_ids, window=args.window) if pf_ids else None
-    w_write = write_work(batch)
+    fp8 = args.kv_fp8
+    w_all = attention_work(batch, window=args.window, kv_fp8=fp8)
+    w_dec = attention_work(batch, dec_ids, window=args.window, kv_fp8=fp8) if dec_ids else None
+    w_pf = attention_work(batch, pf_ids, window=args.window, kv_fp8=fp8) if pf_ids else None
+    w_write = write_work(batch, kv_fp8=fp8)
     peak_flops = PEAK_BF16_TFLOPS if batch.dtype == "bf16" else PEAK_F32_TFLOPS
     t_star = max((w_all["bytes"] + w_write["bytes"]) / (PEAK_HBM_GBPS * 1e9), w_all["flops"] / (peak_flops * 1e12))
     value = 100.0 * t_star / (ms_per_step * 1e-3)
@@ -205,7 +232,8 @@ def main() -> int:
     if w_dec is not None and kern_avg["small"] > 0:
         t = kern_avg["small"] * 1e-3
         gbps = w_dec["bytes"] / t / 1e9
-        decode = {"kernel": "small_tile_mfma" if batch.dtype == "bf16" else "small_tile_valu",
+        decode = {"kernel": ("small_tile_mfma_fp8" if fp8 else "small_tile_mfma") if batch.dtype == "bf16"
+                  else "small_tile_valu",
                   "avg_ms": kern_avg["small"], "merge_avg_ms": kern_avg["merge"],
                   "algorithmic_bytes": w_dec["bytes"], "kv_bytes": w_dec["kv_bytes"],
                   "kv_gbps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS,
@@ -229,10 +257,11 @@ def main() -> int:
                 "avg_launch_ms": kern_avg["small"]}
     else:
         gb = w_write["bytes"] / (kern_avg["kv_write"] * 1e-3) / 1e9
-        roof = {"kernel": "kv_copy16", "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        roof = {"kernel": "kv_quant_fp8" if fp8 else "kv_copy16", "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gb / PEAK_HBM_GBPS, "algorithmic_per_launch": w_write["bytes"],
                 "avg_launch_ms": kern_avg["kv_write"]}
-    roof["traffic"] = measured_traffic(dom, args.workload + (f"_window{args.window}" if args.window else ""))
+    roof["traffic"] = measured_traffic(dom, args.workload + (f"_window{args.window}" if args.window else "")
+                                       + ("_fp8" if fp8 else ""))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -240,7 +269,7 @@ def main() -> int:
         # grouped heads fit 16 columns (decodes), and a spread of rows from the longer chunks
         chunk = [r.new * g > PREFILL_MIN_COLS and r.seq_len > 0 for r in batch.requests]
         cpu = cpu_baseline(batch, args.cpu_prefill_rows, [i for i, f in enumerate(chunk) if not f],
-                           [i for i, f in enumerate(chunk) if f], peak_flops, args.window)
+                           [i for i, f in enumerate(chunk) if f], peak_flops, args.window, fp8)
 
     line = {
         "metric": METRIC, "value": value, "unit": "% of MI355X peak", "n_gpus": 1, "steps": args.steps,
@@ -250,6 +279,7 @@ def main() -> int:
                    "num_reqs": batch.num_reqs, "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
                    "head_dim": batch.head_dim, "block_size": batch.block_size, "pool_blocks": batch.num_blocks,
                    "sliding_window": args.window, "launch": "hip_graph" if args.graph else "eager",
+                   "kv_cache_dtype": "fp8_e4m3" if fp8 else batch.dtype,
                    "parallelism": "single-gpu"},
         "step_roofline_ms": t_star * 1e3,
         "step_algorithmic": {"bytes": w_all["bytes"] + w_write["bytes"], "flops": w_all["flops"]},
@@ -314,12 +344,14 @@ def bench_block_copy(args, torch, pk, dev):
     return 0
 
 
-def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0):
+def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0, kv_fp8=False):
     """The oracle (float64 C, OpenMP) timed on the host on a bounded sample of the same step:
     the full KV write, then attention for every decode row and `n_prefill_rows` prefill rows
     spread evenly over the chunk.  Reported in the metric's unit (the sample's roofline time
-    at MI355X peak over the oracle's time), with the raw rates beside it."""
+    at MI355X peak over the oracle's time), with the raw rates beside it.  kv_fp8: the pool
+    is quantized by the oracle's write before the clock starts; the timed write quantizes."""
     import numpy as np
+    import torch
 
     import oracle
     from tests._util import to_np
@@ -328,6 +360,8 @@ def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0):
     flops = 0.0
     touched = set()
     qsl = batch.query_start_loc_host
+    if kv_fp8 and len(dec_ids) > 64:          # the oracle's fp8 gather is slower: 64 decodes, evenly spaced
+        dec_ids = [dec_ids[i] for i in np.linspace(0, len(dec_ids) - 1, 64).round().astype(int)]
     for r in dec_ids:
         mask[qsl[r]:qsl[r + 1]] = 1
     pf_rows = [i for r in pf_ids for i in range(qsl[r], qsl[r + 1])]
@@ -343,23 +377,40 @@ def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0):
                 seen = np.minimum(seen, window)
             flops += 4.0 * batch.num_heads * batch.head_dim * float(np.sum(seen))
     from workloads.accounting import attention_work
-    kv = attention_work(batch, sorted(touched), window=window)["kv_bytes"] if touched else 0.0
+    kv = attention_work(batch, sorted(touched), window=window, kv_fp8=kv_fp8)["kv_bytes"] if touched else 0.0
     nbytes = kv + int(mask.sum()) * batch.num_heads * batch.head_dim * 2 * (2 if batch.dtype == "bf16" else 4)
-    kc, vc = to_np(batch.k_cache).copy(), to_np(batch.v_cache).copy()
     q, k, v = to_np(batch.q), to_np(batch.k), to_np(batch.v)
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    if kv_fp8:
+        # quantize the context slots the sampled requests read (the step's write adds the rest)
+        shape = tuple(batch.k_cache.shape)
+        bs = batch.block_size
+        ctx = np.unique(np.concatenate([np.asarray(batch.requests[r].blocks, np.int64)[np.arange(
+            batch.requests[r].computed) // bs] * bs + np.arange(batch.requests[r].computed) % bs
+            for r in sorted(touched)] + [np.zeros(0, np.int64)]))
+        kc, vc = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+        ks, vs = np.zeros(shape[:3], np.float32), np.zeros(shape[:3], np.float32)
+        flat = lambda t: to_np(t.reshape(-1, *shape[2:])[torch.from_numpy(ctx)])
+        oracle.kv_write_fp8(flat(batch.k_cache), flat(batch.v_cache), ctx, kc, vc, ks, vs, batch.dtype)
+    else:
+        kc, vc = to_np(batch.k_cache).copy(), to_np(batch.v_cache).copy()
+        ks = vs = None
     t0 = time.perf_counter()
-    oracle.kv_write(k, v, batch.slot_mapping.numpy(), kc, vc, batch.dtype, batch.dtype)
+    if kv_fp8:
+        oracle.kv_write_fp8(k, v, batch.slot_mapping.numpy(), kc, vc, ks, vs, batch.dtype)
+    else:
+        oracle.kv_write(k, v, batch.slot_mapping.numpy(), kc, vc, batch.dtype, batch.dtype)
     oracle.paged_attention(q, kc, vc, batch.query_start_loc.numpy(), batch.seq_lens.numpy(),
-                           batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=mask, window=window)
+                           batch.block_table.numpy(), batch.scale, batch.dtype, row_mask=mask, window=window,
+                           k_scale=ks, v_scale=vs)
     secs = time.perf_counter() - t0
     t_star = max(nbytes / (PEAK_HBM_GBPS * 1e9), flops / (peak_flops * 1e12))
     eprint(f"[bench] oracle sample: {int(mask.sum())} rows in {secs:.2f}s on {cores} threads")
     return {"value": 100.0 * t_star / secs, "unit": "% of MI355X peak", "cores": cores, "kind": "oracle",
             "seconds": secs, "flops_per_s": flops / secs, "kv_bytes_per_s": kv / secs,
             "sample": f"KV write of all {batch.num_tokens} tokens + attention of {int(mask.sum())} of "
-                      f"{batch.num_tokens} rows (every decode row, {min(n_prefill_rows, len(pf_rows))} prefill "
-                      f"rows evenly spaced), {batch.name}"}
+                      f"{batch.num_tokens} rows ({len(dec_ids)} decode requests, {min(n_prefill_rows, len(pf_rows))} prefill "
+                      f"rows evenly spaced), {batch.name}" + (" on fp8 E4M3 pools" if kv_fp8 else "")}
 
 
 if __name__ == "__main__":

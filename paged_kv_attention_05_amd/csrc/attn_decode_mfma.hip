@@ -22,10 +22,13 @@
 //                                           LDS transpose read (ds_read_tr16_b64).
 // P is split into bf16 high and low parts (two products) so the probabilities keep ~16
 // bits: cheap here, since the path is bound by HBM, not by the matrix cores.
-// K goes from HBM straight into registers (two sets, ping-pong) and V straight into a
-// per-wave LDS buffer (gfx950 direct loads, two buffers), so the next block is in flight
-// while the current one is computed.  Keys past the split end are read from the last
-// visible key instead (finite data, masked), so no NaN from an unwritten slot enters.
+// bf16 pools: K goes from HBM straight into registers and V straight into a per-wave LDS
+// buffer (gfx950 direct loads), two of each, so the next block is in flight while the
+// current one is computed.  fp8 pools: the codes of K and V go into two register sets
+// (ping-pong) and V is converted into the LDS buffer.  The block
+// table is read with scalar loads (one entry per block), so no wait on a table entry drains
+// the vector loads in flight.  Keys past the split end are read from the last visible key
+// instead (finite data, masked), so no NaN from an unwritten slot enters.
 #include "pa_internal.h"
 
 namespace pa {
@@ -69,6 +72,15 @@ __device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
 
 __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// v of lane i of the lane's quad, for i = 0..3 (DPP quad permutes)
+__device__ __forceinline__ void quad_bcast4(float v, float* r) {
+  const int x = __builtin_bit_cast(int, v);
+  r[0] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x00, 0xf, 0xf, false));
+  r[1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x55, 0xf, 0xf, false));
+  r[2] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xaa, 0xf, 0xf, false));
+  r[3] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xff, 0xf, 0xf, false));
 }
 
 // four fp8 E4M3 codes (one dword) to four bf16 values, exactly (4 significant bits fit in 8)
@@ -139,12 +151,15 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   // Q^T as the B operand: column n, dims 32*kk + 8*G .. +7; a negative scale becomes -q
   const float sl = fmaxf(fabsf(a.scale_log2e), 1e-30f);
   const uint32_t qsign = a.scale_log2e < 0.f ? 0x80008000u : 0u;
+  // dims of k-chunk kk in lane group G (Q and K take the same permutation of the contraction
+  // dim): fp8 lanes hold D/4 contiguous dims, so a lane's K codes are one contiguous run
+  auto kdim = [](int kk, int g4) { return F8 ? (D / 4) * g4 + 8 * kk : 32 * kk + 8 * g4; };
   bf16x8 qf[C::KC];
   {
     const __bf16* qrow = q + ((int64_t)(b + it.tok0 + ni) * a.H + hkv * a.g + h0 + nj) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
-      u32x4 v = col_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * G) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = col_ok ? *(const u32x4*)(qrow + kdim(kk, G)) : u32x4{0u, 0u, 0u, 0u};
       v ^= qsign;
       qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
@@ -158,54 +173,44 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
 
   const int32_t nblk_end = (ke + kBlk - 1) / kBlk;               // one past the last block
   const int32_t blk0 = kb / kBlk + w;
-  // key rows past the split end are read from key ke-1 instead: finite data, masked out
-  auto slot_of_key = [&](int32_t key) -> int64_t {
-    key = key < ke ? key : ke - 1;
-    return (int64_t)table_row[key >> 4] * kBlk + (key & 15);
-  };
-  // K block straight into the A operand (lane: key n, dims 8G + 32kk .. +7)
-  auto load_k = [&](int32_t lb, bf16x8* kr) {
-    const __bf16* kp = kc + slot_of_key(lb * kBlk + n) * row_elems + 8 * G;
-#pragma unroll
-    for (int kk = 0; kk < C::KC; ++kk) kr[kk] = *(const bf16x8*)(kp + 32 * kk);
-  };
-  // V block straight into this wave's LDS buffer: instruction u fills rows RPI*u .. +RPI-1;
-  // lane l takes row RPI*u + l / CHUNKS, slot l % CHUNKS, holding chunk slot ^ vswz(row)
-  auto load_v = [&](int32_t lb, unsigned char* dst) {
-#pragma unroll
-    for (int u = 0; u < C::VLOADS; ++u) {
-      const int r = C::RPI * u + lane / C::CHUNKS;
-      const int chunk = (lane % C::CHUNKS) ^ vswz<D>(r);
-      load_lds16(vc + slot_of_key(lb * kBlk + r) * row_elems + 8 * chunk, dst + u * 1024);
-    }
+  // A block's keys share one table entry: one scalar load per block, read through the
+  // constant address space so that it waits behind no vector load in flight.
+  const __attribute__((address_space(4))) int32_t* trow =
+      (const __attribute__((address_space(4))) int32_t*)table_row;
+  // slot of key j of block lb; keys past the split end read key ke-1 instead (finite data,
+  // masked), which lies in the same block since lb*16 <= ke-1 for every block in the loop
+  auto slot = [&](int32_t tb, int32_t lb, int j) -> int64_t {
+    return (int64_t)tb * kBlk + (min(lb * kBlk + j, ke - 1) & (kBlk - 1));
   };
 
-  // F8 loads: K codes of key n (8 bytes per k-chunk), V codes of row lane/4 (D/4 bytes), and
-  // the scales of the lane's four S^T keys 4G .. 4G+3
-  constexpr int VB = D / 4;                                   // V bytes per lane and block
-  struct F8Block { u32x2 k[C::KC]; u32x4 v[VB / 16]; float ks[4], vs[4]; };
-  auto load_f8 = [&](int32_t lb, F8Block& f) {
-    const uint8_t* kp = kc8 + slot_of_key(lb * kBlk + n) * row_elems + 8 * G;
+  // F8: one block of codes in registers.  K: key n, the lane's D/4 contiguous dims (kdim).
+  // V: row lane/4, quarter lane%4 of the row.  Scales: K and V scale of key 4G + n%4 (the
+  // lane's quad broadcasts them to the four keys of its S^T rows).  Every load is an
+  // ordinary vector load, so the compiler waits for exactly the block it is about to use.
+  constexpr int VX = D / 64;                                   // 16-byte pieces of V codes per lane
+  constexpr int KX = D / 64;                                   // 16-byte pieces of K codes per lane
+  struct Blk { u32x4 k[KX]; u32x4 v[VX]; float ks, vs; };
+  auto load_f8 = [&](int32_t lb, Blk& f) {
+    const int32_t tb = trow[lb];
+    const uint8_t* kp = kc8 + slot(tb, lb, n) * row_elems + (D / 4) * G;
 #pragma unroll
-    for (int kk = 0; kk < C::KC; ++kk) f.k[kk] = *(const u32x2*)(kp + 32 * kk);
-    const uint8_t* vp = vc8 + slot_of_key(lb * kBlk + (lane >> 2)) * row_elems + VB * (lane & 3);
+    for (int x = 0; x < KX; ++x) f.k[x] = *(const u32x4*)(kp + 16 * x);
+    const uint8_t* vp = vc8 + slot(tb, lb, lane >> 2) * row_elems + (D / 4) * (lane & 3);
 #pragma unroll
-    for (int x = 0; x < VB / 16; ++x) f.v[x] = *(const u32x4*)(vp + 16 * x);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t sidx = slot_of_key(lb * kBlk + 4 * G + i) * a.Hkv + hkv;
-      f.ks[i] = a.k_scale[sidx];
-      f.vs[i] = a.v_scale[sidx];
-    }
+    for (int x = 0; x < VX; ++x) f.v[x] = *(const u32x4*)(vp + 16 * x);
+    const int64_t si = slot(tb, lb, 4 * G + (n & 3)) * a.Hkv + hkv;
+    f.ks = a.k_scale[si];
+    f.vs = a.v_scale[si];
   };
-  // V codes of one block to bf16 in the wave's LDS buffer, same swizzled rows as the bf16 path
-  auto stage_v = [&](const F8Block& f, unsigned char* dst) {
+  // V codes of one block as bf16 rows in the wave's LDS buffer (16-byte chunk c of row r at
+  // slot c ^ vswz(r), as the direct loads of the bf16 path place them)
+  auto stage_v = [&](const Blk& f, unsigned char* dst) {
     const int r = lane >> 2;
 #pragma unroll
-    for (int x = 0; x < VB / 16; ++x) {
+    for (int x = 0; x < VX; ++x) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int chunk = (VB * (lane & 3) + 16 * x + 8 * hf) / 8;   // 8 elements per chunk
+        const int chunk = (D / 32) * (lane & 3) + 2 * x + hf;
         const u32x2 a0 = fp8x4_to_bf16x4(f.v[x][2 * hf]), a1 = fp8x4_to_bf16x4(f.v[x][2 * hf + 1]);
         *(u32x4*)(dst + r * C::ROW + 16 * (chunk ^ vswz<D>(r))) = u32x4{a0[0], a0[1], a1[0], a1[1]};
       }
@@ -260,56 +265,82 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     }
   };
 
-  // blocks blk0, blk0 + 4, ... of this wave, two at a time: K ping-pongs between two register
-  // sets, V between two LDS buffers; the next block's loads are in flight during each compute
-  bf16x8 kA[C::KC], kB[C::KC];
   if constexpr (F8) {
-    // codes ping-pong between two register sets (plain loads: the compiler waits for them)
-    F8Block fA, fB;
-    auto run = [&](int32_t lb, const F8Block& f, unsigned char* vb) {
+    auto run = [&](int32_t lb, const Blk& f, unsigned char* vb) {
       stage_v(f, vb);
       bf16x8 kr[C::KC];
 #pragma unroll
       for (int kk = 0; kk < C::KC; ++kk) {
-        const u32x2 a0 = fp8x4_to_bf16x4(f.k[kk][0]), a1 = fp8x4_to_bf16x4(f.k[kk][1]);
+        const u32x4 w4 = f.k[kk / 2];
+        const u32x2 a0 = fp8x4_to_bf16x4(w4[2 * (kk & 1)]), a1 = fp8x4_to_bf16x4(w4[2 * (kk & 1) + 1]);
         kr[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
       }
-      compute(lb, kr, vb, f.ks, f.vs);
+      float ks[4], vs[4];
+      quad_bcast4(f.ks, ks);
+      quad_bcast4(f.vs, vs);
+      compute(lb, kr, vb, ks, vs);
     };
-    if (blk0 < nblk_end) load_f8(blk0, fA);
-    for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
-      if (lb + 4 < nblk_end) load_f8(lb + 4, fB);
-      run(lb, fA, vbuf0);
-      if (lb + 4 >= nblk_end) break;
-      if (lb + 8 < nblk_end) load_f8(lb + 8, fA);
-      run(lb + 4, fB, vbuf0 + C::VBUF);
+    // this wave's blocks blk0, blk0 + 4, ... through two register sets: the loads of the next
+    // block are issued before each block is computed (a third set measured slower).  They are
+    // unconditional (past the wave's last block they re-read it, from cache), so that every
+    // path through the loop has the same loads in flight and the compiler's waits stay partial.
+    constexpr int NSET = 2;
+    if (blk0 < nblk_end) {
+      const int32_t last = blk0 + 4 * ((nblk_end - 1 - blk0) / 4);   // this wave's last block
+      Blk f[NSET];
+#pragma unroll
+      for (int s = 0; s < NSET - 1; ++s) load_f8(min(blk0 + 4 * s, last), f[s]);
+      bool more = true;
+      for (int32_t lb = blk0; more; lb += 4 * NSET) {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+          const int32_t cur = lb + 4 * s;
+          load_f8(min(cur + 4 * (NSET - 1), last), f[(s + NSET - 1) % NSET]);
+          run(cur, f[s], vbuf0 + (s & 1) * C::VBUF);
+          if (cur >= last) {
+            more = false;
+            break;
+          }
+        }
+      }
     }
   } else {
-  if (blk0 < nblk_end) {
-    load_k(blk0, kA);
-    load_v(blk0, vbuf0);
-  }
-  for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
-    const bool has1 = lb + 4 < nblk_end;
-    if (has1) {
-      load_k(lb + 4, kB);
-      load_v(lb + 4, vbuf0 + C::VBUF);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb landed
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // K block into registers, V block straight into the wave's LDS buffer (gfx950 direct
+    // loads); two of each, ping-pong.  The explicit waits make block lb land before it is
+    // computed (the compiler adds a full wait for direct loads before the LDS reads).
+    auto load_direct = [&](int32_t lb, bf16x8* kr, unsigned char* dst) {
+      const int32_t tb = trow[lb];
+      const __bf16* kp = kc + slot(tb, lb, n) * row_elems + 8 * G;
+#pragma unroll
+      for (int kk = 0; kk < C::KC; ++kk) kr[kk] = *(const bf16x8*)(kp + 32 * kk);
+#pragma unroll
+      for (int u = 0; u < C::VLOADS; ++u) {
+        const int r = C::RPI * u + lane / C::CHUNKS;
+        const int chunk = (lane % C::CHUNKS) ^ vswz<D>(r);
+        load_lds16(vc + slot(tb, lb, r) * row_elems + 8 * chunk, dst + u * 1024);
+      }
+    };
+    const float ones[4] = {1.f, 1.f, 1.f, 1.f};
+    bf16x8 kA[C::KC], kB[C::KC];
+    if (blk0 < nblk_end) load_direct(blk0, kA, vbuf0);
+    for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
+      const bool has1 = lb + 4 < nblk_end;
+      if (has1) {
+        load_direct(lb + 4, kB, vbuf0 + C::VBUF);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute(lb, kA, vbuf0, ones, ones);
+      if (!has1) break;
+      if (lb + 8 < nblk_end) {
+        load_direct(lb + 8, kA, vbuf0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb+4 landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      compute(lb + 4, kB, vbuf0 + C::VBUF, ones, ones);
     }
-    compute(lb, kA, vbuf0, nullptr, nullptr);
-    if (!has1) break;
-    const bool has2 = lb + 8 < nblk_end;
-    if (has2) {
-      load_k(lb + 8, kA);
-      load_v(lb + 8, vbuf0);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb+4 landed
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    compute(lb + 4, kB, vbuf0 + C::VBUF, nullptr, nullptr);
-  }
   }
 
   // combine the four waves: per column max, sum and output

@@ -39,14 +39,17 @@ def _live_slots(batch, req_ids: Iterable[int], window: int = 0) -> int:
     return len(slots)
 
 
-def attention_work(batch, req_ids: Optional[Iterable[int]] = None, window: int = 0) -> Dict[str, float]:
+def attention_work(batch, req_ids: Optional[Iterable[int]] = None, window: int = 0,
+                   kv_fp8: bool = False) -> Dict[str, float]:
     """Algorithmic bytes and flops of paged attention over the given requests (default: all),
-    with a sliding window of `window` tokens (0: none)."""
+    with a sliding window of `window` tokens (0: none).  kv_fp8: the pools hold one-byte E4M3
+    codes plus a float32 scale per (slot, KV head) and tensor; q and out keep the batch dtype."""
     ids = list(range(len(batch.requests))) if req_ids is None else list(req_ids)
     e = ELEM_BYTES[batch.dtype]
     H, Hkv, D = batch.num_heads, batch.num_kv_heads, batch.head_dim
     rows = sum(batch.requests[r].new for r in ids)
-    kv = _live_slots(batch, ids, window) * Hkv * D * e * 2
+    slot_bytes = Hkv * (D + 4) if kv_fp8 else Hkv * D * e
+    kv = _live_slots(batch, ids, window) * slot_bytes * 2
     qo = rows * H * D * e * 2
     meta = sum(4 * (len(batch.requests[r].blocks) + 2) for r in ids)
     scores = 0
@@ -62,9 +65,11 @@ def attention_work(batch, req_ids: Optional[Iterable[int]] = None, window: int =
             "bytes": float(kv + qo + meta), "flops": flops, "rows": rows, "scores_per_head": scores}
 
 
-def write_work(batch) -> Dict[str, float]:
-    """Bytes the KV write must move: read k and v, write them into the pool, read the slots."""
+def write_work(batch, kv_fp8: bool = False) -> Dict[str, float]:
+    """Bytes the KV write must move: read k and v, write them into the pool, read the slots.
+    kv_fp8: the pool row is one code byte per element plus a float32 scale per KV head."""
     e = ELEM_BYTES[batch.dtype]
     n = batch.num_tokens
     row = batch.num_kv_heads * batch.head_dim * e
-    return {"bytes": float(2 * n * row * 2 + 8 * n)}
+    stored = batch.num_kv_heads * (batch.head_dim + 4) if kv_fp8 else row
+    return {"bytes": float(2 * n * (row + stored) + 8 * n)}
