@@ -149,10 +149,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
       small_keys += (double)pa::small_key_span(p, L) * ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
   }
   // Key splits: enough workgroups to fill 256 compute units several times over, but at
-  // most 1024 keys per split so long contexts are cut into balanced pieces.
+  // most 2048 keys per split so long contexts are cut into balanced pieces (1024 measured
+  // slower: more partials to write and merge for the same reads).
   const double target = small_keys * Hkv / 2048.0;
   int32_t split = 64;
-  while (split < 1024 && (double)split * 2 <= target) split *= 2;
+  while (split < 2048 && (double)split * 2 <= target) split *= 2;
   p.split_keys = split;
 
   int64_t ns = 0, nm = 0, np = 0;
