@@ -231,6 +231,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
   float m = kNegInf, lsum = 0.f;
+  float lsum2 = 0.f;                                          // a second row-sum accumulator
   const int G = lane >> 4, i16 = lane & 15;
 
   // S^T of one K tile (keys 64j .. 64j+63, two halves of 32 keys)
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       }
     }
   }
-  auto qk = [&](int b, f32x16* s) {
+  auto qk = [&](int b, f32x16* s, auto&& after_group) {
     // K reads in groups of two k-chunks (four reads), each group issued one group ahead of
     // its products; scheduling fences keep that order
     auto read_k = [&](int g, bf16x8* ka) {
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], f32x16{}, 0, 0, 0)
                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], s[sh], 0, 0, 0);
       }
+      after_group(g);                                  // vector work issued under the products
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -295,11 +297,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   //
   // Slots (barrier-separated): A runs M(i) in slot 2i and X(i) in slot 2i+1; B runs M(i) in
   // slot 2i+1 and X(i) in slot 2i+2.  Tile i lives in ring slot i % 3.  K tile i is read in
-  // slots 2i and 2i+1.  V tile i is converted to fp16 in slot 2i (by every wave) and read in
-  // slots 2i+2 and 2i+3.  At the start of slot 2i every wave issues its share of V(i+1), then
-  // of K(i+2) (their ring slots were last read in slot 2i-1).  The end of slot 2i+1 waits
-  // until only the K(i+2) loads may still be in flight (vmcnt counts in issue order): V(i+1)
-  // is converted in slot 2i+2, K(i+2) gets four slots before slot 2i+4 reads it.
+  // slots 2i and 2i+1.  V tile i is converted to fp16 during M(i) (group A's half in slot 2i,
+  // group B's in slot 2i+1) and read in slots 2i+2 and 2i+3.  At the start of slot 2i every
+  // wave issues its share of V(i+1), then of K(i+2) (their ring slots were last read in slot
+  // 2i-1).  The end of slot 2i+1 waits until only the K(i+2) loads may still be in flight
+  // (vmcnt counts in issue order): V(i+1) is converted in slots 2i+2 and 2i+3, K(i+2) gets
+  // four slots before slot 2i+4 reads it.
   auto vbuf = [&](int b) { return smem + V_RING + b * C::TILE; };
   auto kbuf = [&](int b) { return smem + K_RING + b * C::TILE; };
   const bool grp_a = w < WAVES / 2;                          // uniform
@@ -334,28 +337,38 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // V tile i to fp16 (ring slot P), two 16-byte chunks per thread.  bf16 values convert to
   // fp16 exactly when |v| <= 65504 (fp16's largest finite value; values below 2^-14 become
   // fp16 subnormals, off by at most 2^-25).  A value out of that range (or an infinity) marks
-  // the item for the bf16 kernel.
+  // the item for the bf16 kernel.  Each wave converts its threads' chunks during its own
+  // matrix phase of tile i: the LDS reads go out at the start of the phase and the arithmetic
+  // and stores run in four slices, one after each group of QK^T products, so they issue while
+  // the matrix core works.
   bool wide_seen = false;                                    // wave-uniform
-  auto convert_v = [&](int32_t i, auto par) {
+  u32x4 cv_src[2], cv_dst[2];
+  float cv_amax = 0.f;
+  auto conv_begin = [&](auto par) {
     constexpr int P = decltype(par)::value;
     if constexpr (F16) {
-      if (i >= ntiles) return;
-      float amax = 0.f;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t off = (uint32_t)(P * C::TILE + 16 * (tid + NT * e));
-        const u32x4 src = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_addr(smem + V_RING) + off);
-        u32x4 dst;
+      for (int e = 0; e < 2; ++e)
+        cv_src[e] = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
+            lds_addr(smem + V_RING) + (uint32_t)(P * C::TILE + 16 * (tid + NT * e)));
+      cv_amax = 0.f;
+    }
+  };
+  auto conv_slice = [&](int g, auto par) {
+    constexpr int P = decltype(par)::value;
+    if constexpr (F16) {
+      const int e = g >> 1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(src[k] << 16), hi = __uint_as_float(src[k] & 0xffff0000u);
-          amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
-          const f16x2 hv = {(_Float16)lo, (_Float16)hi};
-          dst[k] = __builtin_bit_cast(uint32_t, hv);
-        }
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_addr(smem + V16_RING) + off) = dst;
+      for (int k = 2 * (g & 1); k < 2 * (g & 1) + 2; ++k) {
+        const float lo = __uint_as_float(cv_src[e][k] << 16), hi = __uint_as_float(cv_src[e][k] & 0xffff0000u);
+        cv_amax = fmaxf(cv_amax, fmaxf(fabsf(lo), fabsf(hi)));
+        const f16x2 hv = {(_Float16)lo, (_Float16)hi};
+        cv_dst[e][k] = __builtin_bit_cast(uint32_t, hv);
       }
-      wide_seen |= __builtin_amdgcn_ballot_w64(amax > 65504.f) != 0;
+      if (g & 1)
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(
+            lds_addr(smem + V16_RING) + (uint32_t)(P * C::TILE + 16 * (tid + NT * e))) = cv_dst[e];
+      if (g == 3) wide_seen |= __builtin_amdgcn_ballot_w64(cv_amax > 65504.f) != 0;
     }
   };
 
@@ -374,6 +387,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   };
   auto phase_m = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
+    if (i < ntiles) conv_begin(par);
     // PV first: P(i-1) is dead before S(i) is produced, so the two share registers
     if (i >= 1) {
       // O^T += V^T P^T over the four 16-key chunks, per chunk one product per d tile (two in
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (i < ntiles) qk(P, s);
+    if (i < ntiles) qk(P, s, [&](int g) { conv_slice(g, par); });
   };
   auto phase_x = [&](int32_t i) {
     if (i >= ntiles) return;
@@ -444,6 +458,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;   // m may be -inf
       m = m_new;
       lsum *= alpha;
+      lsum2 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
     }
@@ -461,7 +476,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
             // rounded values, so the output is an exact convex combination of V rows whose
             // weights are off by at most 2^-12 (relative)
             const f16x2 pr = {(_Float16)p0, (_Float16)p1};
-            lsum += (float)pr[0] + (float)pr[1];
+            // one dot product with (1, 1) adds both rounded values into a float32 sum (the
+            // products are exact); two accumulators halve the dependency chain
+            const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+            if (jj & 2) lsum2 = __builtin_amdgcn_fdot2(pr, ones, lsum2, false);
+            else lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
             pb[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, pr);
           } else {
             lsum += p0 + p1;
@@ -483,22 +502,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   auto step = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
     using Pn = std::integral_constant<int, (P + 1) % NBUF>;
-    if (grp_a) {
-      issue_slot(i, par);
-      convert_v(i, par);
-    }
+    if (grp_a) issue_slot(i, par);
     phase_m(i, par);
     if (grp_a) bar(); else bar_loads(i);
-    if (!grp_a) {
-      issue_slot(i + 1, Pn{});
-      convert_v(i + 1, Pn{});
-    }
+    if (!grp_a) issue_slot(i + 1, Pn{});
     phase_x(i);
     if (grp_a) bar_loads(i); else bar();
   };
   if (!grp_a) {
     issue_slot(0, P0{});
-    convert_v(0, P0{});
     bar();
   }
   for (int32_t i = 0; i <= ntiles; i += 3) {
@@ -512,6 +524,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   }
 
   // normalise and stage the tile's output rows in LDS, then write them out coalesced
+  lsum += lsum2;
   lsum += __shfl_xor(lsum, 32);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   __syncthreads();                                          // all waves done with the K/V tiles (the
