@@ -142,14 +142,30 @@ int oracle_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mappin
                         uint8_t* v_cache, float* k_scale, float* v_scale, int64_t num_tokens,
                         int32_t num_kv_heads, int32_t head_dim, int64_t num_slots, int32_t in_dtype) {
     const int64_t row = (int64_t)num_kv_heads * head_dim;
+    for (int64_t i = 0; i < num_tokens; ++i)
+        if (slot_mapping[i] >= num_slots) return -1;
+    /* Rows with a slot of their own are independent (distinct slots are a precondition of
+     * write_kv) and are quantized in parallel; every padding row targets the last slot, where
+     * the last padding row in order is the one that stays, so only that one is written. */
+    #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < num_tokens; ++i) {
-        const int64_t s = slot_mapping[i] >= 0 ? slot_mapping[i] : num_slots - 1;
-        if (s >= num_slots) return -1;
+        if (slot_mapping[i] < 0) continue;
+        const int64_t s = slot_mapping[i];
         for (int32_t h = 0; h < num_kv_heads; ++h) {
             const int64_t src = i * row + (int64_t)h * head_dim, dst = s * row + (int64_t)h * head_dim;
             quantize_row(k, src, head_dim, in_dtype, k_cache + dst, k_scale + s * num_kv_heads + h);
             quantize_row(v, src, head_dim, in_dtype, v_cache + dst, v_scale + s * num_kv_heads + h);
         }
+    }
+    for (int64_t i = num_tokens - 1; i >= 0; --i) {
+        if (slot_mapping[i] >= 0) continue;
+        const int64_t s = num_slots - 1;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            const int64_t src = i * row + (int64_t)h * head_dim, dst = s * row + (int64_t)h * head_dim;
+            quantize_row(k, src, head_dim, in_dtype, k_cache + dst, k_scale + s * num_kv_heads + h);
+            quantize_row(v, src, head_dim, in_dtype, v_cache + dst, v_scale + s * num_kv_heads + h);
+        }
+        break;
     }
     return 0;
 }
