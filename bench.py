@@ -213,7 +213,7 @@ def main() -> int:
     # algorithmic work, split the way the library routes requests
     g = batch.num_heads // batch.num_kv_heads
     prefill_capable = batch.dtype == "bf16" and batch.block_size == 16 and batch.head_dim == 128 \
-        and 256 % g == 0 and not args.kv_fp8
+        and 256 % g == 0
     is_pf = [prefill_capable and r.new * g > PREFILL_MIN_COLS and r.seq_len > 0 for r in batch.requests]
     if kern["prefill"][1] == 0:          # the library routed every request to the small tiles
         is_pf = [False] * len(is_pf)
@@ -242,13 +242,15 @@ def main() -> int:
     if w_pf is not None and kern_avg["prefill"] > 0:
         t = kern_avg["prefill"] * 1e-3
         tf = w_pf["flops"] / t / 1e12
-        prefill = {"kernel": "prefill_tile_mfma", "avg_ms": kern_avg["prefill"], "algorithmic_flops": w_pf["flops"],
+        # (fp8 pools: the staging copy of the prefill requests' blocks and the kernel on it)
+        prefill = {"kernel": "stage_fp8 + prefill_tile_mfma_fp8" if fp8 else "prefill_tile_mfma",
+                   "avg_ms": kern_avg["prefill"], "algorithmic_flops": w_pf["flops"],
                    "algorithmic_bytes": w_pf["bytes"], "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
 
     # dominant kernel: the one taking the most time per step
     dom = max(("prefill", "small", "kv_write"), key=lambda n: kern_avg[n])
     if dom == "prefill":
-        roof = {"kernel": "prefill_tile_mfma", "bound": "mfma", "achieved": prefill["tflops"],
+        roof = {"kernel": prefill["kernel"], "bound": "mfma", "achieved": prefill["tflops"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": prefill["frac_mfma"],
                 "algorithmic_per_launch": w_pf["flops"], "avg_launch_ms": kern_avg["prefill"]}
     elif dom == "small":

@@ -128,8 +128,9 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
   p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
   const bool auto_path = g_path == 0;
-  p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && !fp8 && pa::prefill_mfma_supported(D, bs, p.g))
+  p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
                     ? pa::prefill_tile_tokens(p.g) : 0;
+  p.f8 = fp8 ? 1 : 0;
   p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs)) ? 1 : 0;
   if (fp8 && p.decode_kind != 1)
     return fail(PA_ERR_DTYPE, "fp8 pools need dtype bf16, block_size 16, head_dim 64 or 128 and the automatic path");
@@ -156,15 +157,21 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   while (split < 2048 && (double)split * 2 <= target) split *= 2;
   p.split_keys = split;
 
-  int64_t ns = 0, nm = 0, np = 0;
+  int64_t ns = 0, nm = 0, np = 0, ng = 0;
+  int32_t stage_w = 0;
   for (int32_t r = 0; r < R; ++r) {
     int32_t a, b, c, d;
     pa::request_counts(p, qsl[r + 1] - qsl[r], lens[r], &a, &b, &c, &d);
     ns += a; nm += b; np += c;
+    const int32_t st = pa::staged_blocks(p, qsl[r + 1] - qsl[r], lens[r]);
+    ng += st;
+    stage_w = std::max(stage_w, st);
   }
-  if (ns > INT32_MAX / 2 || nm > INT32_MAX / 2 || np > INT32_MAX / 2)
+  if (ns > INT32_MAX / 2 || nm > INT32_MAX / 2 || np > INT32_MAX / 2 || ng > INT32_MAX / 2)
     return fail(PA_ERR_SHAPE, "batch too large for the work lists");
-  p.n_small = ns; p.n_merge = nm; p.n_pf = np;
+  // the prefill kernel addresses staged scales with 32-bit offsets per workgroup
+  if (ng * 2 * Hkv * 16 * 4 > (int64_t)INT32_MAX) return fail(PA_ERR_SHAPE, "fp8 prefill: too many staged blocks");
+  p.n_small = ns; p.n_merge = nm; p.n_pf = np; p.n_stage = ng; p.stage_w = stage_w;
 
   size_t off = 0;
   p.off_req = off;   off = align_up(off + sizeof(pa::ReqOffsets) * (size_t)(R + 1), 256);
@@ -176,6 +183,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.off_pm = off;    off = align_up(off + 4 * nparts, 256);
   p.off_pl = off;    off = align_up(off + 4 * nparts, 256);
   p.off_pacc = off;  off = align_up(off + 4 * nparts * (size_t)D, 256);
+  // fp8 pools: staged bf16 codes, scales and block table of the prefill requests
+  p.off_f8_tab = off; off = align_up(off + 4 * (size_t)(ng > 0 ? R : 0) * stage_w, 256);
+  p.off_f8_k = off;   off = align_up(off + 2 * (size_t)ng * bs * Hkv * D, 256);
+  p.off_f8_v = off;   off = align_up(off + 2 * (size_t)ng * bs * Hkv * D, 256);
+  p.off_f8_s = off;   off = align_up(off + 4 * (size_t)ng * 2 * Hkv * bs, 256);
   p.total_bytes = off;
   *out = p;
   return PA_OK;
@@ -408,7 +420,10 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
 
   hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
   if (e == hipSuccess && p.n_pf > 0)
-    e = timed(PA_KIND_PREFILL, stream, [&] { return pa::launch_prefill_mfma(p, a, workspace, stream); });
+    e = timed(PA_KIND_PREFILL, stream, [&] {
+      return p.f8 ? pa::launch_stage_fp8(p, a, std::max(std::fabs(a.scale_log2e), 1e-30f), workspace, stream)
+                  : pa::launch_prefill_mfma(p, a, workspace, stream);
+    });
   if (e == hipSuccess && p.n_small > 0)
     e = timed(PA_KIND_SMALL, stream, [&] {
       return p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)

@@ -83,13 +83,6 @@ __device__ __forceinline__ void quad_bcast4(float v, float* r) {
   r[3] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xff, 0xf, 0xf, false));
 }
 
-// four fp8 E4M3 codes (one dword) to four bf16 values, exactly (4 significant bits fit in 8)
-__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  const bf16x4 r = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)hi[0], (__bf16)hi[1]};
-  return __builtin_bit_cast(u32x2, r);
-}
-
 // F8: the pools hold fp8 E4M3 codes with a float32 scale per (slot, KV head) (a.k_scale,
 // a.v_scale).  K codes convert exactly to bf16 for the QK^T product and each score is then
 // multiplied by its key's scale; V codes convert exactly to bf16 into the wave's LDS buffer,

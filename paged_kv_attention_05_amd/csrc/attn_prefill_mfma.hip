@@ -51,6 +51,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -108,13 +109,27 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, unsi
                : "memory");
 }
 
+// 4 bytes per lane from global memory straight into LDS at lds_wave_base + 4 * lane (the
+// same conventions as load_lds16)
+__device__ __forceinline__ void load_lds4(const void* g, unsigned char* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds_wave_base)), "v"(g) : "memory");
+}
+
 // F16 = true: the fast kernel.  V tiles are converted to fp16 in LDS and P goes to the matrix
 // cores as fp16; a workgroup that meets a V value outside fp16's range (|v| > 65504) flags
 // its item (wide[lin] = 1) and its output is rewritten by the F16 = false kernel, launched
 // right after on the same stream, which keeps V in bf16 and carries P as a bf16 pair.
-template <int D, int WAVES, bool F16>
+//
+// F8 = true (with F16 = false): fp8 pools.  The kernel reads the staged bf16 copy of the
+// request's codes (exact) through the staged block table, and the staged per-key scales:
+// each score is multiplied by its key's K scale (which carries |scale| log2 e) and each
+// probability by its key's V scale before the PV product (the row sum takes the
+// probabilities alone), as the gathered rows of "ReferenceBackend.dequantize" are the codes
+// times their scales.  Scales of a tile come into LDS with its V loads (waves 0 and 1).
+template <int D, int WAVES, bool F16, bool F8>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnArgs a, const PfItem* __restrict__ items,
                                                                             int32_t n_items, int32_t* __restrict__ wide) {
+  static_assert(!(F16 && F8), "fp8 pools run the bf16-V kernel");
   using C = PrefillCfg<D>;
   constexpr int ROWS = 32 * WAVES;
   constexpr int NT = 64 * WAVES;
@@ -122,8 +137,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // and K.  The output staging reuses the first bytes.
   constexpr int NBUF = 3;
   constexpr int V16_RING = 0, V_RING = F16 ? NBUF * C::TILE : 0, K_RING = V_RING + NBUF * C::TILE;
+  constexpr int SC_RING = K_RING + NBUF * C::TILE;            // F8: per tile 64 K then 64 V scales
+  constexpr int SC_TILE = F8 ? 2 * kBK * 4 : 0;
   constexpr int OUT_BYTES = ROWS * C::ROW;
-  constexpr int SMEM = (K_RING + NBUF * C::TILE) > OUT_BYTES ? (K_RING + NBUF * C::TILE) : OUT_BYTES;
+  constexpr int SMEM = (SC_RING + NBUF * SC_TILE) > OUT_BYTES ? (SC_RING + NBUF * SC_TILE) : OUT_BYTES;
   __shared__ __align__(1024) unsigned char smem[SMEM];
 
   // workgroup -> (item, KV head): consecutive items of one head on one XCD (workgroups are
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int32_t per_xcd = (total + 7) / 8;
   const int32_t lin = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
   if (lin >= total) return;
-  if constexpr (!F16) {
+  if constexpr (!F16 && !F8) {
     if (__builtin_amdgcn_readfirstlane(wide[lin]) == 0) return;   // the fast kernel's output stands
   }
   const int hkv = lin / n_items;
@@ -226,6 +243,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   };
   auto issue_k = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(kc, j, bl, dst); };
   auto issue_v = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(vc, j, bl, dst); };
+  // F8: the 64 K scales (wave 0) and V scales (wave 1) of tile j, one per lane, into the ring
+  // slot at dst (K scales at +0, V scales at +256); staged layout [block][2][Hkv][16]
+  auto issue_sc = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
+    if constexpr (F8) {
+      if (w >= 2) return;
+      j += t0;
+      int32_t kg = j * kBK + lane, blk;
+      if (j * kBK + kBK <= kend) {
+        const int bi = lane >> 4;
+        blk = bi == 0 ? bl.b0 : bi == 1 ? bl.b1 : bi == 2 ? bl.b2 : bl.b3;
+      } else {
+        kg = min(kg, kend - 1);
+        blk = table_row[kg >> 4];
+      }
+      load_lds4(a.k_scale + (((int64_t)blk * 2 + w) * a.Hkv + hkv) * 16 + (kg & 15), dst + 256 * w);
+    }
+  };
 
   f32x16 o[C::DT];
 #pragma unroll
@@ -260,6 +294,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       }
     }
   }
+  // F8: per-lane base of the scale reads (this lane's keys start at 4h in each 8-key run);
+  // the ring slot, the K/V half and the key run are immediates
+  uint32_t scoff = lds_addr(smem + SC_RING) + 16 * h;
+  asm volatile("" : "+v"(scoff));
   auto qk = [&](int b, f32x16* s, auto&& after_group) {
     // K reads in groups of two k-chunks (four reads), each group issued one group ahead of
     // its products; scheduling fences keep that order
@@ -305,6 +343,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // four slots before slot 2i+4 reads it.
   auto vbuf = [&](int b) { return smem + V_RING + b * C::TILE; };
   auto kbuf = [&](int b) { return smem + K_RING + b * C::TILE; };
+  auto scbuf = [&](int b) { return smem + SC_RING + b * SC_TILE; };
   const bool grp_a = w < WAVES / 2;                          // uniform
   auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   static_assert(UK == 2, "the wait counts below assume two load instructions per tile and wave");
@@ -319,6 +358,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     const Blocks bl0 = fetch_blocks(0), bl1 = fetch_blocks(1);
     issue_k(0, bl0, kbuf(0));
     issue_v(0, bl0, vbuf(0));
+    issue_sc(0, bl0, scbuf(0));
     if (ntiles > 1) issue_k(1, bl1, kbuf(1));
   }
   Blocks blV = fetch_blocks(1);                              // blocks of V(i+1)
@@ -328,7 +368,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // three), so all LDS addresses are per-lane offsets plus immediates
   auto issue_slot = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
-    if (i + 1 < ntiles) issue_v(i + 1, blV, vbuf((P + 1) % NBUF));
+    if (i + 1 < ntiles) {
+      issue_v(i + 1, blV, vbuf((P + 1) % NBUF));
+      issue_sc(i + 1, blV, scbuf((P + 1) % NBUF));         // before K(i+2): the waits count K last
+    }
     if (i + 2 < ntiles) issue_k(i + 2, blK, kbuf((P + 2) % NBUF));
     blV = blK;
     blK = fetch_blocks(i + 3);
@@ -423,8 +466,26 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     }
     if (i < ntiles) qk(P, s, [&](int g) { conv_slice(g, par); });
   };
-  auto phase_x = [&](int32_t i) {
+  auto phase_x = [&](int32_t i, auto par) {
+    constexpr int P = decltype(par)::value;
     if (i >= ntiles) return;
+    if constexpr (F8) {
+      // scores times their keys' K scales (score r of this lane is key 32sh + 8(r/4) + 4h + r%4
+      // of the tile), before the mask so that a masked score is -inf whatever the scale
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 k4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(
+              scoff + P * SC_TILE + 4 * (32 * sh + 8 * q));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[sh][4 * q + e] *= k4[e];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);                   // keep the scale reads' registers short-lived
+    }
+    // the factor from scores to base-2 exponents (F8: already in the K scales)
+    const float slx = F8 ? 1.f : sl;
     // causal mask on the diagonal tiles, window mask on the tiles holding some row's window
     // start; masked scores are -inf before the max.  This lane's score r is key kt + off + 4h.
     const int32_t kt = (i + t0) * kBK;
@@ -451,7 +512,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[sh][r], s[sh][r + 1]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * sl;                              // mx is finite or -inf, sl > 0
+    const float mxs = mx * slx;                             // mx is finite or -inf, slx > 0
     // move the reference only when the row max grew by more than kLazy (or it is unset)
     if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {
       const float m_new = mxs > m + kLazy ? mxs : m;
@@ -467,10 +528,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
+        // F8: the V scales of this group's eight keys (two 4-key runs)
+        f32x4 vsc[2];
+        if constexpr (F8) {
+#pragma unroll
+          for (int hq = 0; hq < 2; ++hq)
+            vsc[hq] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(
+                scoff + P * SC_TILE + 256 + 4 * (32 * sh + 8 * (2 * kh + hq)));
+        }
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj], sl, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj + 1], sl, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj], slx, -m_use));
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj + 1], slx, -m_use));
           if constexpr (F16) {
             // rounded to nearest fp16 (p <= 2^kLazy, inside its range); l adds up the same
             // rounded values, so the output is an exact convex combination of V rows whose
@@ -484,13 +553,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
             pb[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, pr);
           } else {
             lsum += p0 + p1;
-            const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
-            const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);
+            float q0 = p0, q1 = p1;
+            if constexpr (F8) {
+              // times the keys' V scales for the PV product (score 8kh + jj is key 32sh +
+              // 8(2kh + jj/4) + 4h + jj%4)
+              q0 *= vsc[jj >> 2][jj & 3];
+              q1 *= vsc[jj >> 2][(jj & 3) + 1];
+            }
+            const uint32_t h0 = __float_as_uint(q0) & 0xffff0000u, h1 = __float_as_uint(q1) & 0xffff0000u;
+            const float r0 = q0 - __uint_as_float(h0), r1 = q1 - __uint_as_float(h1);
             pb[2 * sh + kh][jj >> 1] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);   // {h0.hi16, h1.hi16}
             const bf16x2 lo = {(__bf16)r0, (__bf16)r1};
             pl[2 * sh + kh][jj >> 1] = __builtin_bit_cast(uint32_t, lo);
           }
         }
+        if constexpr (F8) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -506,7 +583,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     phase_m(i, par);
     if (grp_a) bar(); else bar_loads(i);
     if (!grp_a) issue_slot(i + 1, Pn{});
-    phase_x(i);
+    phase_x(i, par);
     if (grp_a) bar_loads(i); else bar();
   };
   if (!grp_a) {
@@ -570,12 +647,17 @@ hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipSt
   int32_t* wide = (int32_t*)((char*)ws + p.off_pf_wide);     // zeroed by the plan kernel
   const int64_t total = p.n_pf * p.Hkv;
   const dim3 grid((unsigned)((total + 7) / 8 * 8));
-  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true>), grid, dim3(64 * kWaves), 0, s, a, items, (int32_t)p.n_pf,
-                     wide);
+  if (p.f8) {   // the staged copy of fp8 pools (launched by launch_stage_fp8)
+    hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false, true>), grid, dim3(64 * kWaves), 0, s, a, items,
+                       (int32_t)p.n_pf, wide);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true, false>), grid, dim3(64 * kWaves), 0, s, a, items,
+                     (int32_t)p.n_pf, wide);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // items whose V left fp16's range (normally none: these workgroups exit at once)
-  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false>), grid, dim3(64 * kWaves), 0, s, a, items,
+  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false, false>), grid, dim3(64 * kWaves), 0, s, a, items,
                      (int32_t)p.n_pf, wide);
   return hipGetLastError();
 }

@@ -32,6 +32,17 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
 };
 
+// four fp8 E4M3 codes (one dword) to four bf16 values, exactly (4 significant bits fit in 8,
+// and every E4M3 exponent is inside bf16's range)
+typedef uint32_t pa_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ pa_u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x4_ __attribute__((ext_vector_type(4)));
+  const f32x2_ lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  const bf16x4_ r = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)hi[0], (__bf16)hi[1]};
+  return __builtin_bit_cast(pa_u32x2, r);
+}
+
 // ---------------------------------------------------------------- work decomposition
 // A "small tile" is up to 16 query columns of one request and one KV head: `tile_tokens`
 // consecutive query rows times `tile_heads` of the KV head's query heads, over one key
@@ -44,9 +55,13 @@ struct Plan {
   int32_t pf_tokens;               // 0: prefill path off
   int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
   int32_t window;                  // sliding window in tokens (0: none)
+  int32_t f8;                      // 1: fp8 pools (prefill requests read a staged bf16 copy)
+  int32_t stage_w;                 // f8: width of the staged block table (blocks per request)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed)
+  int64_t n_stage;                 // f8: staged blocks (all blocks of the prefill requests)
   // workspace layout (byte offsets)
-  size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, total_bytes;
+  size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc;
+  size_t off_f8_tab, off_f8_k, off_f8_v, off_f8_s, total_bytes;
 };
 
 struct alignas(16) SmallItem {
@@ -63,6 +78,7 @@ struct alignas(8) PfItem {
 // per-request offsets written by the planner (exclusive scans)
 struct alignas(16) ReqOffsets {
   int32_t small, merge, pf, nsplit;
+  int32_t stage, pad0, pad1, pad2;     // stage: first staged block of the request (fp8 pools)
 };
 
 // Classification of request r, identical on host and device.  Up to four small tiles (64
@@ -72,6 +88,10 @@ struct alignas(16) ReqOffsets {
 constexpr int kPrefillMinCols = 4 * kCols;
 __host__ __device__ __forceinline__ bool use_prefill_path(const Plan& p, int32_t t, int32_t L) {
   return p.pf_tokens > 0 && L > 0 && (int64_t)t * p.g > kPrefillMinCols;
+}
+// Staged blocks of request r with fp8 pools: every block of a prefill-path request.
+__host__ __device__ __forceinline__ int32_t staged_blocks(const Plan& p, int32_t t, int32_t L) {
+  return (p.f8 && use_prefill_path(p, t, L)) ? (L + p.bs - 1) / p.bs : 0;
 }
 // Keys one small tile of a request with context L can see: all L, or with a sliding window
 // of w tokens at most w + tile_tokens - 1 (the tile's rows are consecutive), plus up to 63
@@ -151,6 +171,9 @@ hipError_t launch_small_valu(const Plan& p, const AttnArgs& a, void* ws, int32_t
 hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
 hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
+// fp8 pools: stage the prefill requests' blocks as bf16 codes and scaled scales, then run the
+// prefill kernel on the staged copy
+hipError_t launch_stage_fp8(const Plan& p, const AttnArgs& a, float scale_abs_log2e, void* ws, hipStream_t s);
 bool small_mfma_supported(int32_t D, int32_t bs);
 bool prefill_mfma_supported(int32_t D, int32_t bs, int32_t g);
 int32_t prefill_tile_tokens(int32_t g);

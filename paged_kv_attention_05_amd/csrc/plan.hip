@@ -50,22 +50,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
   __shared__ int32_t scan[kPlanThreads];
   __shared__ int32_t o_small[kPlanThreads], o_merge[kPlanThreads], o_pf[kPlanThreads];
   __shared__ int32_t c_t[kPlanThreads], c_ns[kPlanThreads];
-  __shared__ int32_t carry[3];
+  __shared__ int32_t carry[4];
   const int tid = threadIdx.x;
   // the prefill kernel's per-workgroup "redo in bf16" flags start cleared every call
   for (int64_t i = tid; i < p.n_pf * p.Hkv; i += kPlanThreads) pf_wide[i] = 0;
-  if (tid == 0) carry[0] = carry[1] = carry[2] = 0;
+  if (tid == 0) carry[0] = carry[1] = carry[2] = carry[3] = 0;
   __syncthreads();
 
   for (int base = 0; base < p.R; base += kPlanThreads) {
     const int r = base + tid;
     const int n = min(kPlanThreads, p.R - base);
-    int32_t ns_small = 0, ns_merge = 0, ns_pf = 0, nsplit = 1, t = 0;
+    int32_t ns_small = 0, ns_merge = 0, ns_pf = 0, nsplit = 1, t = 0, ns_stage = 0;
     if (r < p.R) {
       t = qsl[r + 1] - qsl[r];
       request_counts(p, t, seq_lens[r], &ns_small, &ns_merge, &ns_pf, &nsplit);
+      ns_stage = staged_blocks(p, t, seq_lens[r]);
     }
-    const int32_t cs = carry[0], cm = carry[1], cp = carry[2];
+    const int32_t cs = carry[0], cm = carry[1], cp = carry[2], cg = carry[3];
     const int32_t inc_s = block_scan_inclusive(scan, ns_small);
     const int32_t tot_s = scan[kPlanThreads - 1];
     __syncthreads();
@@ -74,17 +75,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
     __syncthreads();
     const int32_t inc_p = block_scan_inclusive(scan, ns_pf);
     const int32_t tot_p = scan[kPlanThreads - 1];
+    __syncthreads();
+    const int32_t inc_g = block_scan_inclusive(scan, ns_stage);
+    const int32_t tot_g = scan[kPlanThreads - 1];
     o_small[tid] = cs + inc_s - ns_small;
     o_merge[tid] = cm + inc_m - ns_merge;
     o_pf[tid] = cp + inc_p - ns_pf;
     c_t[tid] = t;
     c_ns[tid] = nsplit;
-    if (r < p.R) req[r] = ReqOffsets{o_small[tid], o_merge[tid], o_pf[tid], nsplit};
+    if (r < p.R) req[r] = ReqOffsets{o_small[tid], o_merge[tid], o_pf[tid], nsplit, cg + inc_g - ns_stage, 0, 0, 0};
     __syncthreads();
     if (tid == 0) {
       carry[0] = cs + tot_s;
       carry[1] = cm + tot_m;
       carry[2] = cp + tot_p;
+      carry[3] = cg + tot_g;
     }
     __syncthreads();
 
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
     }
     __syncthreads();
   }
-  if (tid == 0) req[p.R] = ReqOffsets{carry[0], carry[1], carry[2], 0};
+  if (tid == 0) req[p.R] = ReqOffsets{carry[0], carry[1], carry[2], 0, carry[3], 0, 0, 0};
 }
 
 }  // namespace

@@ -187,11 +187,16 @@ def test_kv_write_fp8_parity(in_dtype):
 
 
 FP8 = [
-    # (name, specs, H, Hkv, D, window)
+    # (name, specs, H, Hkv, D, window); chunks over 64 query columns at D=128 take the
+    # prefill kernel on the staged copy, everything else the small tiles
     ("decodes", [(1000, 1), (15, 1), (300, 1), (5000, 1), (0, 1)], 32, 8, 128, 0),
-    ("chunks_on_small_tiles", [(700, 150), (90, 1), (0, 300)], 32, 8, 128, 0),
+    ("chunks", [(700, 150), (90, 1), (0, 300)], 32, 8, 128, 0),
     ("spec_rows_d64", [(100, 2), (57, 3), (300, 4), (16, 5)], 8, 2, 64, 0),
     ("window", [(3000, 1), (200, 40), (9, 1)], 32, 8, 128, 100),
+    ("long_chunk_g8", [(3000, 600), (37, 1), (0, 70)], 64, 8, 128, 0),
+    ("chunk_window", [(2000, 400), (5, 1), (100, 33)], 32, 8, 128, 300),
+    ("chunk_g2_tail", [(33, 200), (64, 64), (1000, 131)], 8, 4, 128, 0),
+    ("chunk_d64_small_tiles", [(500, 300), (0, 77)], 64, 8, 64, 0),
 ]
 
 
@@ -224,6 +229,35 @@ def test_fp8_attention_parity(name, specs, h, hkv, d, window):
     err = attention_error(out.float().cpu().numpy(), ref64, "bf16")
     H.log(f"[parity] fp8_{name}: error {err:.3g} x bound")
     H.record({"case": f"fp8_{name}", "dtype": "bf16", "kv": "fp8_e4m3", "window": window, "error_x_bound": err})
+    assert err <= 1.0, err
+
+
+def test_fp8_long_context_full_size():
+    """The long-context batch (16 decodes at 32768 + a 4096-token chunk at 28672, 64/8
+    heads) on fp8 pools: sampled rows, the chunk through the staged prefill kernel."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    b = workloads.long_context()
+    kc, vc, ks, vs = _fp8_pools(b)
+    g = [torch.from_numpy(x.copy()).to(dev) for x in (kc, vc, ks, vs)]
+    pk.paged_kv_write_fp8(b.k.to(dev), b.v.to(dev), b.slot_mapping.to(dev), *g)
+    out = pk.paged_attention_varlen(b.q.to(dev), g[0], g[1], b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                    b.block_table.to(dev), b.block_size, b.scale,
+                                    query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host,
+                                    k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    oracle.kv_write_fp8(to_np(b.k), to_np(b.v), b.slot_mapping.numpy(), kc, vc, ks, vs, "bf16")
+    mask = _sample_rows(b, 9)
+    _, ref64 = oracle.paged_attention(to_np(b.q), kc, vc, b.query_start_loc.numpy(), b.seq_lens.numpy(),
+                                      b.block_table.numpy(), b.scale, "bf16", want_f64=True, row_mask=mask,
+                                      k_scale=ks, v_scale=vs)
+    rows = np.nonzero(mask)[0]
+    err = attention_error(out.float().cpu().numpy()[rows], ref64[rows], "bf16")
+    H.log(f"[parity] fp8_long_context: error {err:.3g} x bound over {len(rows)} rows")
+    H.record({"case": "fp8_long_context", "dtype": "bf16", "kv": "fp8_e4m3", "rows": int(len(rows)),
+              "error_x_bound": err})
     assert err <= 1.0, err
 
 
