@@ -157,12 +157,14 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   while (split < 2048 && (double)split * 2 <= target) split *= 2;
   p.split_keys = split;
 
-  int64_t ns = 0, nm = 0, np = 0, ng = 0;
+  int64_t ns = 0, nm = 0, np = 0, ng = 0, n1 = 0, n3 = 0;
   int32_t stage_w = 0;
   for (int32_t r = 0; r < R; ++r) {
     int32_t a, b, c, d;
     pa::request_counts(p, qsl[r + 1] - qsl[r], lens[r], &a, &b, &c, &d);
     ns += a; nm += b; np += c;
+    pa::small_groups(p, qsl[r + 1] - qsl[r], lens[r], &a, &b);
+    n1 += a; n3 += b;
     const int32_t st = pa::staged_blocks(p, qsl[r + 1] - qsl[r], lens[r]);
     ng += st;
     stage_w = std::max(stage_w, st);
@@ -172,10 +174,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   // the prefill kernel addresses staged scales with 32-bit offsets per workgroup
   if (ng * 2 * Hkv * 16 * 4 > (int64_t)INT32_MAX) return fail(PA_ERR_SHAPE, "fp8 prefill: too many staged blocks");
   p.n_small = ns; p.n_merge = nm; p.n_pf = np; p.n_stage = ng; p.stage_w = stage_w;
+  p.n_g1 = n1; p.n_g3 = n3;
 
   size_t off = 0;
   p.off_req = off;   off = align_up(off + sizeof(pa::ReqOffsets) * (size_t)(R + 1), 256);
-  p.off_small = off; off = align_up(off + sizeof(pa::SmallItem) * (size_t)ns, 256);
+  p.off_small = off; off = align_up(off + sizeof(pa::SmallItem) * (size_t)(p.decode_kind == 1 ? 0 : ns), 256);
   p.off_merge = off; off = align_up(off + sizeof(pa::MergeItem) * (size_t)nm, 256);
   p.off_pf = off;    off = align_up(off + sizeof(pa::PfItem) * (size_t)np, 256);
   p.off_pf_wide = off; off = align_up(off + sizeof(int32_t) * (size_t)np * Hkv, 256);
@@ -183,6 +186,9 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.off_pm = off;    off = align_up(off + 4 * nparts, 256);
   p.off_pl = off;    off = align_up(off + 4 * nparts, 256);
   p.off_pacc = off;  off = align_up(off + 4 * nparts * (size_t)D, 256);
+  const bool mfma_lists = p.decode_kind == 1;
+  p.off_g1 = off;    off = align_up(off + sizeof(pa::SmallItem) * (size_t)(mfma_lists ? n1 : 0), 256);
+  p.off_g3 = off;    off = align_up(off + sizeof(pa::SmallItem) * (size_t)(mfma_lists ? n3 : 0), 256);
   // fp8 pools: staged bf16 codes, scales and block table of the prefill requests
   p.off_f8_tab = off; off = align_up(off + 4 * (size_t)(ng > 0 ? R : 0) * stage_w, 256);
   p.off_f8_k = off;   off = align_up(off + 2 * (size_t)ng * bs * Hkv * D, 256);

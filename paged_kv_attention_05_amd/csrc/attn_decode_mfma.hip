@@ -88,9 +88,15 @@ __device__ __forceinline__ void quad_bcast4(float v, float* r) {
 // multiplied by its key's scale; V codes convert exactly to bf16 into the wave's LDS buffer,
 // and each probability is multiplied by its key's V scale before the PV product (the row sum
 // takes the probabilities alone), so sum_j p_j (s_j v8_j) = sum_j (p_j s_j) v8_j.
-template <int D, bool F8>
-__global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
-                                                       Partials part) {
+//
+// NC > 1: the workgroup takes up to NC consecutive 16-column tiles of one request (a request
+// with more than 16 query columns per KV head: speculative-verification rows, short chunks)
+// over one key split, and every K/V block it reads serves all of them: each tile keeps its
+// own Q^T, running max, sum and O^T, and the V^T transpose reads are shared.  Tiles of one
+// item share the split's key range, which holds without a sliding window.
+template <int D, bool F8, int NC>
+__global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
+                                                                       int32_t total_idx, Partials part) {
   using C = DecodeCfg<D>;
   // per wave: two V buffers; after the key loop the same bytes hold the per-wave output slabs
   constexpr int kVBytes = 4 * 2 * C::VBUF;
@@ -100,40 +106,59 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
 
   const int32_t item = blockIdx.x;
   const int hkv = blockIdx.y;
-  if (item >= __builtin_amdgcn_readfirstlane(a.totals[0])) return;
+  if (item >= __builtin_amdgcn_readfirstlane(a.totals[total_idx])) return;
   SmallItem it = items[item];
   // the item is the same for the whole workgroup: scalar registers, scalar loop bounds
   it.r = __builtin_amdgcn_readfirstlane(it.r);
-  it.tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
-  it.hsub = __builtin_amdgcn_readfirstlane(it.hsub);
   it.split = __builtin_amdgcn_readfirstlane(it.split);
   it.nsplit = __builtin_amdgcn_readfirstlane(it.nsplit);
+  it.first = __builtin_amdgcn_readfirstlane(it.first);
+  const int32_t tile0 = __builtin_amdgcn_readfirstlane(it.tile0);
+  const int32_t ntile = NC == 1 ? 1 : __builtin_amdgcn_readfirstlane(it.ntile);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave id: uniform
   const int n = lane & 15, G = lane >> 4;
   const int32_t b = __builtin_amdgcn_readfirstlane(a.qsl[it.r]);
   const int32_t t = __builtin_amdgcn_readfirstlane(a.qsl[it.r + 1]) - b;
   const int32_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[it.r]), c = L - t;
-  const int32_t Tn = min(a.tile_tokens, t - it.tok0);
-  const int32_t h0 = it.hsub * a.tile_heads;
-  const int32_t HGn = min(a.tile_heads, a.g - h0);
   const __bf16* q = (const __bf16*)a.q;
   __bf16* out = (__bf16*)a.out;
+  // tile u of the item: its first token, head subset, token and head counts
+  const int hsubs = (a.g + a.tile_heads - 1) / a.tile_heads;
+  int32_t tok0[NC], h0[NC], Tn[NC], HGn[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int32_t tl = tile0 + u;
+    tok0[u] = (tl / hsubs) * a.tile_tokens;
+    h0[u] = (tl % hsubs) * a.tile_heads;
+    Tn[u] = u < ntile ? min(a.tile_tokens, t - tok0[u]) : 0;
+    HGn[u] = min(a.tile_heads, a.g - h0[u]);
+  }
 
   if (L <= 0) {   // padding request: zero rows
-    for (int e = threadIdx.x; e < kCols * D; e += 256) {
-      const int col = e / D, d = e - col * D;
-      const int i = col / a.tile_heads, j = col - i * a.tile_heads;
-      if (i < Tn && j < HGn) out[((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d] = (__bf16)0.f;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      for (int e = threadIdx.x; e < kCols * D; e += 256) {
+        const int col = e / D, d = e - col * D;
+        const int i = col / a.tile_heads, j = col - i * a.tile_heads;
+        if (i < Tn[u] && j < HGn[u]) out[((int64_t)(b + tok0[u] + i) * a.H + hkv * a.g + h0[u] + j) * D + d] = (__bf16)0.f;
+      }
     }
     return;
   }
 
   const int ni = n / a.tile_heads, nj = n - ni * a.tile_heads;
-  const bool col_ok = ni < Tn && nj < HGn;
-  const int32_t pos = c + it.tok0 + ni;
-  const int32_t lo = a.window > 0 ? pos - a.window : -1;        // keys <= lo are outside the window
-  const int32_t kb = small_key_base(a.window, c + it.tok0) + it.split * a.split_keys;   // multiple of 64
-  const int32_t ke = min(c + it.tok0 + Tn, kb + a.split_keys);
+  bool col_ok[NC];
+  int32_t pos[NC], ke_u[NC];
+  const int32_t kb = small_key_base(a.window, c + tok0[0]) + it.split * a.split_keys;   // multiple of 64
+  int32_t ke = 0;                                               // one past the last key of any tile
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    col_ok[u] = ni < Tn[u] && nj < HGn[u];
+    pos[u] = c + tok0[u] + ni;
+    ke_u[u] = u < ntile ? min(c + tok0[u] + Tn[u], kb + a.split_keys) : 0;
+    ke = max(ke, ke_u[u]);
+  }
+  const int32_t lo = a.window > 0 ? pos[0] - a.window : -1;     // keys <= lo are outside the window (NC == 1)
   const int32_t* table_row = a.block_table + (int64_t)it.r * a.stride;
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const __bf16* kc = (const __bf16*)a.k_cache + (int64_t)hkv * D;
@@ -147,22 +172,28 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   // dims of k-chunk kk in lane group G (Q and K take the same permutation of the contraction
   // dim): fp8 lanes hold D/4 contiguous dims, so a lane's K codes are one contiguous run
   auto kdim = [](int kk, int g4) { return F8 ? (D / 4) * g4 + 8 * kk : 32 * kk + 8 * g4; };
-  bf16x8 qf[C::KC];
-  {
-    const __bf16* qrow = q + ((int64_t)(b + it.tok0 + ni) * a.H + hkv * a.g + h0 + nj) * D;
+  bf16x8 qf[NC][C::KC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const __bf16* qrow = q + ((int64_t)(b + tok0[u] + ni) * a.H + hkv * a.g + h0[u] + nj) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
-      u32x4 v = col_ok ? *(const u32x4*)(qrow + kdim(kk, G)) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = col_ok[u] ? *(const u32x4*)(qrow + kdim(kk, G)) : u32x4{0u, 0u, 0u, 0u};
       v ^= qsign;
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
+      qf[u][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
   unsigned char* vbuf0 = smem + w * 2 * C::VBUF;
-  f32x4 o[C::DT];
+  f32x4 o[NC][C::DT];
+  float m[NC], lsum[NC];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.f;
+  for (int u = 0; u < NC; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[u] = kNegInf;
+    lsum[u] = 0.f;
+  }
 
   const int32_t nblk_end = (ke + kBlk - 1) / kBlk;               // one past the last block
   const int32_t blk0 = kb / kBlk + w;
@@ -211,50 +242,59 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
   };
 
   auto compute = [&](int32_t lb, const bf16x8* kcur, const unsigned char* vb, const float* ks, const float* vs) {
-    // S^T = K Q^T
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < C::KC; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kk], qf[kk], s, 0, 0, 0);
-    if constexpr (F8) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] *= ks[i];
-    }
-    // masked scores, running max (base 2)
     const int32_t key0 = lb * kBlk + 4 * G;
-    float sv[4];
+    float alpha[NC];
+    bf16x4 phi[NC], plo[NC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sv[i] = (col_ok && key0 + i < ke && key0 + i <= pos && key0 + i > lo) ? s[i] : kNegInf;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * sl);
-    const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;   // m may be -inf
-    m = m_new;
-    const float m_use = m == kNegInf ? 0.f : m;
-    float p[4];
+    for (int u = 0; u < NC; ++u) {
+      if (u >= ntile) break;
+      // S^T = K Q^T
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl, -m_use));
-    lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-    if constexpr (F8) {
+      for (int kk = 0; kk < C::KC; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kk], qf[u][kk], s, 0, 0, 0);
+      if constexpr (F8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] *= vs[i];
+        for (int i = 0; i < 4; ++i) s[i] *= ks[i];
+      }
+      // masked scores, running max (base 2)
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sv[i] = (col_ok[u] && key0 + i < ke_u[u] && key0 + i <= pos[u] && key0 + i > lo) ? s[i] : kNegInf;
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[u], mx * sl);
+      alpha[u] = m_new > m[u] ? __builtin_amdgcn_exp2f(m[u] - m_new) : 1.f;   // m may be -inf
+      m[u] = m_new;
+      const float m_use = m[u] == kNegInf ? 0.f : m[u];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl, -m_use));
+      lsum[u] = lsum[u] * alpha[u] + (p[0] + p[1]) + (p[2] + p[3]);
+      if constexpr (F8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] *= vs[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        phi[u][i] = (__bf16)p[i];
+        plo[u][i] = (__bf16)(p[i] - (float)phi[u][i]);
+      }
     }
-    bf16x4 phi, plo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      phi[i] = (__bf16)p[i];
-      plo[i] = (__bf16)(p[i] - (float)phi[i]);
-    }
-    // O^T = alpha * O^T + V^T P^T
+    // O^T = alpha * O^T + V^T P^T (one transpose read per d tile serves every tile)
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      o[dt] *= alpha;
       const int r = 4 * G + (n >> 2);
       const int chunk = 2 * dt + ((n & 3) >> 1);
       const bf16x4 vt = tr_read(vb + r * C::ROW + 16 * (chunk ^ vswz<D>(r)) + 8 * (n & 1));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        if (u >= ntile) break;
+        o[u][dt] *= alpha[u];
+        o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[u], o[u][dt], 0, 0, 0);
+        o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo[u], o[u][dt], 0, 0, 0);
+      }
     }
   };
 
@@ -336,62 +376,82 @@ __global__ __launch_bounds__(256, 3) void small_tile_mfma(AttnArgs a, const Smal
     }
   }
 
-  // combine the four waves: per column max, sum and output
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (G == 0) {
-    sM[w][n] = m;
-    sL[w][n] = lsum;
-  }
-  __syncthreads();   // also: every wave is done with its V buffers
-  float M = kNegInf;
-#pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sM[ww][n]);
-  const float M_use = M == kNegInf ? 0.f : M;
-  const float f_own = __builtin_amdgcn_exp2f(m - M_use);
-  if (w == 0 && G == 0) {
-    float tot = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) tot += sL[ww][n] * __builtin_amdgcn_exp2f(sM[ww][n] - M_use);
-    sTot[n] = tot;
-    sMax[n] = M;
-  }
+  // combine the four waves, one tile after another: per column max, sum and output
   float* slab = (float*)smem;                 // [4][16 cols][D]
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+  for (int u = 0; u < NC; ++u) {
+    if (u >= ntile) break;
+    float ls = lsum[u];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    if (G == 0) {
+      sM[w][n] = m[u];
+      sL[w][n] = ls;
+    }
+    __syncthreads();   // also: every wave is done with its V buffers (tile 0) or with the
+                       // previous tile's slab (later tiles)
+    float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) slab[(w * kCols + n) * D + 16 * dt + 4 * G + i] = o[dt][i] * f_own;
-  }
-  __syncthreads();
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sM[ww][n]);
+    const float M_use = M == kNegInf ? 0.f : M;
+    const float f_own = __builtin_amdgcn_exp2f(m[u] - M_use);
+    if (w == 0 && G == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) tot += sL[ww][n] * __builtin_amdgcn_exp2f(sM[ww][n] - M_use);
+      sTot[n] = tot;
+      sMax[n] = M;
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) slab[(w * kCols + n) * D + 16 * dt + 4 * G + i] = o[u][dt][i] * f_own;
+    }
+    __syncthreads();
 
-  // each thread finishes 8 consecutive dims of one column
-  constexpr int kPer = 8;
-  for (int e = threadIdx.x * kPer; e < kCols * D; e += 256 * kPer) {
-    const int col = e / D, d = e - col * D;
-    const int i = col / a.tile_heads, j = col - i * a.tile_heads;
-    if (i >= Tn || j >= HGn) continue;
-    float acc[kPer];
+    // each thread finishes 8 consecutive dims of one column; split-K partials go to the
+    // tile's own slot (tile-split index first + u * nsplit + split), which the merge reads
+    const int64_t ts = (int64_t)it.first + (int64_t)u * it.nsplit + it.split;
+    constexpr int kPer = 8;
+    for (int e = threadIdx.x * kPer; e < kCols * D; e += 256 * kPer) {
+      const int col = e / D, d = e - col * D;
+      const int i = col / a.tile_heads, j = col - i * a.tile_heads;
+      if (i >= Tn[u] || j >= HGn[u]) continue;
+      float acc[kPer];
 #pragma unroll
-    for (int x = 0; x < kPer; ++x)
-      acc[x] = slab[(0 * kCols + col) * D + d + x] + slab[(1 * kCols + col) * D + d + x] +
-               slab[(2 * kCols + col) * D + d + x] + slab[(3 * kCols + col) * D + d + x];
-    if (it.nsplit == 1) {
-      const float inv = 1.f / sTot[col];
-      bf16x8 r;
+      for (int x = 0; x < kPer; ++x)
+        acc[x] = slab[(0 * kCols + col) * D + d + x] + slab[(1 * kCols + col) * D + d + x] +
+                 slab[(2 * kCols + col) * D + d + x] + slab[(3 * kCols + col) * D + d + x];
+      if (it.nsplit == 1) {
+        const float inv = 1.f / sTot[col];
+        bf16x8 r;
 #pragma unroll
-      for (int x = 0; x < kPer; ++x) r[x] = (__bf16)(acc[x] * inv);
-      *(bf16x8*)(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d) = r;
-    } else {
-      const int64_t pi = ((int64_t)item * a.Hkv + hkv) * kCols + col;
-      float4* dst = (float4*)(part.acc + pi * D + d);
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      if (d == 0) {
-        part.m[pi] = sMax[col];
-        part.l[pi] = sTot[col];
+        for (int x = 0; x < kPer; ++x) r[x] = (__bf16)(acc[x] * inv);
+        *(bf16x8*)(out + ((int64_t)(b + tok0[u] + i) * a.H + hkv * a.g + h0[u] + j) * D + d) = r;
+      } else {
+        const int64_t pi = (ts * a.Hkv + hkv) * kCols + col;
+        float4* dst = (float4*)(part.acc + pi * D + d);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if (d == 0) {
+          part.m[pi] = sMax[col];
+          part.l[pi] = sTot[col];
+        }
       }
     }
+    if (u + 1 < ntile) __syncthreads();   // the next tile reuses sM, sTot and the slab
   }
+}
+
+template <int NC, bool F8>
+hipError_t launch_small_nc(const Plan& p, const AttnArgs& a, const SmallItem* items, int64_t n_items, int32_t total_idx,
+                           Partials part, hipStream_t s) {
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_items, (unsigned)p.Hkv);
+  if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
+  else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -401,16 +461,18 @@ bool small_mfma_supported(int32_t D, int32_t bs) { return bs == kBlk && (D == 64
 hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s) {
   if (p.n_small == 0) return hipSuccess;
   char* w = (char*)ws;
-  const SmallItem* items = (const SmallItem*)(w + p.off_small);
   Partials part{(float*)(w + p.off_pm), (float*)(w + p.off_pl), (float*)(w + p.off_pacc)};
-  const dim3 grid((unsigned)p.n_small, (unsigned)p.Hkv);
-  const bool f8 = a.k_scale != nullptr;
-  if (p.D == 128 && !f8) hipLaunchKernelGGL((small_tile_mfma<128, false>), grid, dim3(256), 0, s, a, items, part);
-  else if (p.D == 64 && !f8) hipLaunchKernelGGL((small_tile_mfma<64, false>), grid, dim3(256), 0, s, a, items, part);
-  else if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, true>), grid, dim3(256), 0, s, a, items, part);
-  else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, true>), grid, dim3(256), 0, s, a, items, part);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  // single tiles (decodes), then the groups of tiles of wider requests
+  const SmallItem* single = (const SmallItem*)(w + p.off_g1);
+  const SmallItem* grouped = (const SmallItem*)(w + p.off_g3);
+  if (a.k_scale != nullptr) {   // fp8 pools: single tiles only
+    if (p.n_g3 != 0) return hipErrorInvalidValue;
+    return launch_small_nc<1, true>(p, a, single, p.n_g1, kTotalG1, part, s);
+  }
+  if (group_tiles(p) != kGroupTiles) return hipErrorInvalidValue;
+  hipError_t e = launch_small_nc<1, false>(p, a, single, p.n_g1, kTotalG1, part, s);
+  if (e != hipSuccess) return e;
+  return launch_small_nc<kGroupTiles, false>(p, a, grouped, p.n_g3, kTotalG3, part, s);
 }
 
 }  // namespace pa

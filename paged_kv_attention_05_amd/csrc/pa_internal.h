@@ -57,16 +57,18 @@ struct Plan {
   int32_t window;                  // sliding window in tokens (0: none)
   int32_t f8;                      // 1: fp8 pools (prefill requests read a staged bf16 copy)
   int32_t stage_w;                 // f8: width of the staged block table (blocks per request)
-  int64_t n_small, n_merge, n_pf;  // item counts (host-computed)
+  int64_t n_small, n_merge, n_pf;  // item counts (host-computed); n_small counts tile-splits
+  int64_t n_g1, n_g3;              // matrix-core small kernels: single-tile and grouped items
   int64_t n_stage;                 // f8: staged blocks (all blocks of the prefill requests)
   // workspace layout (byte offsets)
-  size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc;
+  size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, off_g1, off_g3;
   size_t off_f8_tab, off_f8_k, off_f8_v, off_f8_s, total_bytes;
 };
 
 struct alignas(16) SmallItem {
   int32_t r, tok0, hsub, split;
-  int32_t nsplit, first, pad0, pad1;   // first: index of the tile's split 0 (partials base)
+  int32_t nsplit, first;   // first: tile-split index of the (first) tile's split 0 (partials base)
+  int32_t tile0, ntile;    // the item's first tile of its request and its tile count
 };
 struct alignas(16) MergeItem {
   int32_t r, tok0, hsub, first;
@@ -78,8 +80,12 @@ struct alignas(8) PfItem {
 // per-request offsets written by the planner (exclusive scans)
 struct alignas(16) ReqOffsets {
   int32_t small, merge, pf, nsplit;
-  int32_t stage, pad0, pad1, pad2;     // stage: first staged block of the request (fp8 pools)
+  int32_t stage;                       // first staged block of the request (fp8 pools)
+  int32_t g1, g3;                      // offsets in the matrix-core small kernels' two item lists
+  int32_t pad0;
 };
+// indices into the request offsets seen as int32 (the totals row req[R])
+constexpr int kTotalSmall = 0, kTotalMerge = 1, kTotalPf = 2, kTotalG1 = 5, kTotalG3 = 6;
 
 // Classification of request r, identical on host and device.  Up to four small tiles (64
 // query columns: decodes, speculative-verification rows, short chunks) stay on the small
@@ -126,6 +132,24 @@ __host__ __device__ __forceinline__ void request_counts(const Plan& p, int32_t t
   *nsplit = ns;
   *n_small = tiles * ns;
   *n_merge = ns > 1 ? tiles : 0;
+}
+
+// The matrix-core small kernel's items: a request with one 16-column tile (a decode), or any
+// request under a sliding window, gets one item per tile and key split; a wider request
+// (speculative-verification rows, short chunks) gets one item per group of up to
+// kGroupTiles consecutive tiles and key split, which reads each K/V block once for the group.
+// (kGroupTiles tiles with bf16 pools; none with fp8 pools, whose kernel measured slower with
+// the registers of a second tile than re-reading the codes)
+constexpr int kGroupTiles = 3;
+__host__ __device__ __forceinline__ int32_t group_tiles(const Plan& p) { return p.f8 ? 1 : kGroupTiles; }
+__host__ __device__ __forceinline__ void small_groups(const Plan& p, int32_t t, int32_t L, int32_t* n1, int32_t* n3) {
+  *n1 = *n3 = 0;
+  if (t <= 0 || use_prefill_path(p, t, L)) return;
+  const int32_t tiles = ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+  const int32_t ns = small_nsplit(p, L);
+  const int32_t gt = group_tiles(p);
+  if (tiles == 1 || gt == 1 || p.window > 0 || L <= 0) *n1 = tiles * ns;
+  else *n3 = ((tiles + gt - 1) / gt) * ns;
 }
 
 // Arguments common to the attention kernels.

@@ -130,6 +130,9 @@ EDGE = [
     ("prefill_g1_long_context", [(3000, 129)], 8, 8, 128, 16, "bf16"),
     ("prefill_g16_d64", [(100, 9), (0, 3)], 32, 2, 64, 16, "bf16"),
     ("prefill_outliers", [(700, 150), (90, 1)], 32, 8, 128, 16, "bf16"),
+    # grouped small tiles with two head subsets per token (g = 32): groups cross tokens
+    ("groups_two_head_subsets", [(70, 1), (5, 9), (300, 4), (2100, 2)], 32, 1, 64, 16, "bf16"),
+    ("groups_g4_spec_splits", [(5000, 9), (2047, 5), (2049, 9), (100, 3)], 16, 4, 128, 16, "bf16"),
 ]
 
 
