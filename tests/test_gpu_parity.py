@@ -376,21 +376,31 @@ def test_copy_blocks_debug_checks():
 
 
 # ------------------------------------------------------------------------- graph capture
-def test_graph_captured_decode_step_replays():
-    """A padded decode batch (13 requests + 3 padding rows, pad_to of "Flattened ragged
-    batches") captured once in a HIP graph as KV write + attention sized for seq_len <= 2048,
-    then replayed on four batches with other lengths, tables and values copied into the
-    captured buffers.  Every replay matches the oracle, and the same call made eagerly with
-    the same sizing gives the same bits; eager work and synchronisations run between replays."""
+GRAPH = [
+    # (name, query rows of the 13 requests, padded request count: padding requests have one
+    # row, slot -1 and seq_len 0)
+    ("decodes", [1] * 13, 16),
+    ("spec_rows", [2, 3, 5, 9] * 3 + [2], 16),     # 1 + k rows: single and grouped tiles
+]
+
+
+@pytest.mark.parametrize("name,rows,pad", GRAPH, ids=[g_[0] for g_ in GRAPH])
+def test_graph_captured_decode_step_replays(name, rows, pad):
+    """A padded batch of 13 requests (pad_to of "Flattened ragged batches") captured once in
+    a HIP graph as KV write + attention sized for seq_len <= 2048, then replayed on four
+    batches with other lengths, tables and values copied into the captured buffers.  Every
+    replay matches the oracle, and the same call made eagerly with the same sizing gives the
+    same bits; eager work and synchronisations run between replays."""
     import paged_kv_attention_05_amd as pk
     dev = torch.device("cuda:0")
-    MAX, NB, R, W = 2048, 2100, 16, 2048 // 16
+    MAX, NB, W = 2048, 2100, 2048 // 16
+    R = pad
     rng = np.random.default_rng(61)
 
     def batch(seed):
-        lens = rng.integers(1, MAX, size=13)
-        return workloads.small_batch([(int(L) - 1, 1) for L in lens], dtype="bf16", num_heads=32, num_kv_heads=8,
-                                     head_dim=128, num_blocks=NB, seed=seed, pad_to=R)
+        lens = [int(rng.integers(t, MAX)) for t in rows]
+        return workloads.small_batch([(L - t, t) for L, t in zip(lens, rows)], dtype="bf16", num_heads=32,
+                                     num_kv_heads=8, head_dim=128, num_blocks=NB, seed=seed, pad_to=pad)
 
     def table_of(b):
         t = torch.zeros((R, W), dtype=torch.int32)
@@ -442,7 +452,7 @@ def test_graph_captured_decode_step_replays():
         assert torch.equal(st["kc"].cpu().view(torch.int16)[:-1], kc2.cpu().view(torch.int16)[:-1])
         ref64, _, _ = H.oracle_step(b)
         err = attention_error(got.float().numpy(), ref64, "bf16")
-        H.log(f"[parity] graph replay {i}: error {err:.3g} x bound")
+        H.log(f"[parity] graph {name} replay {i}: error {err:.3g} x bound")
         assert err <= 1.0, (i, err)
 
 
