@@ -137,6 +137,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
 
   // pass 1: validate and measure the small-tile work to size the key splits
   double small_keys = 0;
+  int32_t span_max = 0;
   for (int32_t r = 0; r < R; ++r) {
     const int32_t t = qsl[r + 1] - qsl[r];
     const int32_t L = lens[r];
@@ -146,15 +147,21 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
       return fail(PA_ERR_METADATA, "request " + std::to_string(r) + " has more query rows than its seq_len");
     if ((int64_t)(L + bs - 1) / bs > stride)
       return fail(PA_ERR_METADATA, "block_table_stride too small for seq_len of request " + std::to_string(r));
-    if (t > 0 && L > 0 && !pa::use_prefill_path(p, t, L))
+    if (t > 0 && L > 0 && !pa::use_prefill_path(p, t, L)) {
       small_keys += (double)pa::small_key_span(p, L) * ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+      span_max = std::max(span_max, pa::small_key_span(p, L));
+    }
   }
   // Key splits: enough workgroups to fill 256 compute units several times over, but at
   // most 2048 keys per split so long contexts are cut into balanced pieces (1024 measured
   // slower: more partials to write and merge for the same reads).
+  // A small batch would get many short splits that way, and merging their partials then
+  // costs more than the attention (16 decodes of <= 2048 keys: 64-key splits, a 21 us merge):
+  // splits also grow until no tile has more than 8.
   const double target = small_keys * Hkv / 2048.0;
   int32_t split = 64;
   while (split < 2048 && (double)split * 2 <= target) split *= 2;
+  while (split < 2048 && (int64_t)split * 8 < span_max) split *= 2;
   p.split_keys = split;
 
   int64_t ns = 0, nm = 0, np = 0, ng = 0, n1 = 0, n3 = 0;
