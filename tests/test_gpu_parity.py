@@ -235,6 +235,45 @@ def test_fp8_attention_parity(name, specs, h, hkv, d, window):
     assert err <= 1.0, err
 
 
+def _fp8_step(b, window=0):
+    """KV write + attention on fp8 pools (the oracle's quantization of the batch's context
+    pool); returns (GPU out, float64 oracle out) for every row."""
+    import oracle
+    import paged_kv_attention_05_amd as pk
+    from tests._util import to_np
+    dev = torch.device("cuda:0")
+    kc, vc, ks, vs = _fp8_pools(b)
+    g = [torch.from_numpy(x.copy()).to(dev) for x in (kc, vc, ks, vs)]
+    pk.paged_kv_write_fp8(b.k.to(dev), b.v.to(dev), b.slot_mapping.to(dev), *g)
+    out = pk.paged_attention_varlen(b.q.to(dev), g[0], g[1], b.query_start_loc.to(dev), b.seq_lens.to(dev),
+                                    b.block_table.to(dev), b.block_size, b.scale,
+                                    query_start_loc_host=b.query_start_loc_host, seq_lens_host=b.seq_lens_host,
+                                    sliding_window=window, k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    oracle.kv_write_fp8(to_np(b.k), to_np(b.v), b.slot_mapping.numpy(), kc, vc, ks, vs, "bf16")
+    _, ref64 = oracle.paged_attention(to_np(b.q), kc, vc, b.query_start_loc.numpy(), b.seq_lens.numpy(),
+                                      b.block_table.numpy(), b.scale, "bf16", want_f64=True, window=window,
+                                      k_scale=ks, v_scale=vs)
+    return out.float().cpu().numpy(), ref64
+
+
+@pytest.mark.parametrize("scale", [-0.11, 0.0])
+def test_negative_and_zero_scale_every_path(scale):
+    """A negative softmax scale (applied as |scale| on -q) and a zero scale (uniform weights
+    over the visible keys), through the prefill kernel, single and grouped small tiles, and
+    both on fp8 pools (the staged K scales carry |scale| log2 e)."""
+    specs = [(700, 150), (90, 1), (300, 9), (2000, 5), (0, 1)]
+    b = workloads.small_batch(specs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128, seed=83)
+    b.scale = scale
+    H.check_batch(b, label=f"scale_{scale}")
+    b8 = workloads.small_batch(specs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128, seed=84)
+    b8.scale = scale
+    got, ref64 = _fp8_step(b8)
+    err = attention_error(got, ref64, "bf16")
+    H.log(f"[parity] fp8 scale {scale}: error {err:.3g} x bound")
+    assert err <= 1.0, err
+
+
 def test_fp8_long_context_full_size():
     """The long-context batch (16 decodes at 32768 + a 4096-token chunk at 28672, 64/8
     heads) on fp8 pools: sampled rows, the chunk through the staged prefill kernel."""
