@@ -81,6 +81,8 @@ def main() -> int:
                          "pool is quantized once before the steps, each step writes its tokens through the "
                          "quantizing write and attends over the codes (bf16 batches; every request on the "
                          "small tiles)")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the streaming read / copy probe of the achievable HBM bandwidth")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once: a plain copy "
                          "of known size whose HBM counters scale the kernels' counters")
@@ -206,6 +208,18 @@ def main() -> int:
         torch.cuda.synchronize()
         ms_per_step = start.elapsed_time(end) / args.steps
         eprint(f"[bench] graph replays: {ms_per_step:.4f} ms/step (eager {eager_ms:.4f})")
+    # per-step spread: the same steps again, each between its own events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        if args.graph:
+            graph.replay()
+        else:
+            step()
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    spread = {"median_ms": per_step[len(per_step) // 2], "min_ms": per_step[0], "max_ms": per_step[-1]}
     kern_avg = {name: (tot / cnt if cnt else 0.0) for name, (tot, cnt) in kern.items()}
     eprint(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernels (avg ms): "
            + ", ".join(f"{n}={t:.4f}" for n, t in kern_avg.items() if t))
@@ -265,6 +279,35 @@ def main() -> int:
     roof["traffic"] = measured_traffic(dom, args.workload + (f"_window{args.window}" if args.window else "")
                                        + ("_fp8" if fp8 else ""))
 
+    # mixed batches: the decode-row and the prefill-row requests as sub-calls of their own
+    # (attention only, over the pool the steps wrote)
+    subcalls = None
+    if dec_ids and pf_ids and not args.graph:
+        subcalls = {}
+        for name, ids, w_sub in (("decode", dec_ids, w_dec), ("prefill", pf_ids, w_pf)):
+            sub = _subset(torch, batch, ids, q, qsl.device)
+            o_sub = torch.empty_like(sub["q"])
+
+            def call():
+                pk.paged_attention_varlen(sub["q"], kc, vc, sub["qsl"], sub["lens"], sub["table"], batch.block_size,
+                                          batch.scale, o_sub, query_start_loc_host=sub["qsl_host"],
+                                          seq_lens_host=sub["lens_host"], sliding_window=args.window,
+                                          k_scale=ks, v_scale=vs)
+            for _ in range(args.warmup):
+                call()
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(args.steps):
+                call()
+            end.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(end) / args.steps
+            subcalls[name] = {"requests": len(ids), "ms": ms, "algorithmic_bytes": w_sub["bytes"],
+                              "algorithmic_flops": w_sub["flops"], "gbps": w_sub["bytes"] / (ms * 1e-3) / 1e9,
+                              "tflops": w_sub["flops"] / (ms * 1e-3) / 1e12}
+
+    hbm = None if args.no_hbm_probe else hbm_probe(torch, pk, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         # the oracle's sample is chosen by request shape: every row of requests whose rows times
@@ -290,6 +333,9 @@ def main() -> int:
                      "gbps": w_write["bytes"] / (kern_avg["kv_write"] * 1e-3) / 1e9 if kern_avg["kv_write"] else None},
         "kernels_avg_ms": kern_avg,
         "eager_ms_per_step": eager_ms,
+        "step_spread": spread,
+        "subcalls": subcalls,
+        "hbm_probe": hbm,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -344,6 +390,66 @@ def bench_block_copy(args, torch, pk, dev):
             "cpu_baseline": None}
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _subset(torch, batch, ids, q, dev):
+    """Device tensors of the requests `ids` alone: their rows of q, query_start_loc, seq_lens
+    and block-table rows."""
+    qh = batch.query_start_loc_host
+    rows = torch.cat([torch.arange(qh[r], qh[r + 1]) for r in ids]).to(dev)
+    starts = [0]
+    for r in ids:
+        starts.append(starts[-1] + qh[r + 1] - qh[r])
+    lens = [batch.seq_lens_host[r] for r in ids]
+    return {"q": q.index_select(0, rows).contiguous(),
+            "qsl": torch.tensor(starts, dtype=torch.int32, device=dev),
+            "lens": torch.tensor(lens, dtype=torch.int32, device=dev),
+            "table": batch.block_table[ids].contiguous().to(dev), "qsl_host": starts, "lens_host": lens}
+
+
+def hbm_probe(torch, pk, dev, gib=4):
+    """Achievable HBM rates beside the 8 TB/s specification: the library's streaming-read
+    probe over `gib` GiB (best over a sweep of grid sizes, best of 5 each) and a torch
+    device-to-device copy of the same size (read + write)."""
+    n = (gib << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        times = []
+        for _ in range(5):
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return min(times)
+    nbytes = n * 4
+    reads = {grid: nbytes / (best(lambda: pk.hbm_read_probe(x, sink, grid)) * 1e-3) / 1e9
+             for grid in (1024, 2048, 4096, 8192)}
+    copy_ms = best(lambda: y.copy_(x))
+    del x, y
+    torch.cuda.empty_cache()
+    top = max(reads, key=reads.get)
+    return {"bytes": nbytes, "read_gbps": reads[top], "read_grid": top,
+            "read_gbps_by_grid": {str(k): v for k, v in reads.items()},
+            "copy_gbps_read_plus_write": 2 * nbytes / (copy_ms * 1e-3) / 1e9,
+            "how": "paged_hbm_read_probe (nontemporal 16-byte loads, 256 threads per workgroup) over 4 GiB, "
+                   "and torch copy_ of 4 GiB; best of 5"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0, kv_fp8=False):
@@ -409,6 +515,7 @@ def cpu_baseline(batch, n_prefill_rows, dec_ids, pf_ids, peak_flops, window=0, k
     t_star = max(nbytes / (PEAK_HBM_GBPS * 1e9), flops / (peak_flops * 1e12))
     eprint(f"[bench] oracle sample: {int(mask.sum())} rows in {secs:.2f}s on {cores} threads")
     return {"value": 100.0 * t_star / secs, "unit": "% of MI355X peak", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "seconds": secs, "flops_per_s": flops / secs, "kv_bytes_per_s": kv / secs,
             "sample": f"KV write of all {batch.num_tokens} tokens + attention of {int(mask.sum())} of "
                       f"{batch.num_tokens} rows ({len(dec_ids)} decode requests, {min(n_prefill_rows, len(pf_rows))} prefill "

@@ -259,6 +259,18 @@ void paged_attn_set_path(int32_t path);
 void paged_attn_set_timing(int32_t enable);
 int paged_attn_timing_report(double* total_ms, int32_t* count, int32_t n_kinds);
 
+/*
+ * paged_hbm_read_probe (measurement only, not part of the attention path): reads `bytes`
+ * bytes of device memory at `buf` once, with a grid of `grid` workgroups of 256 threads, so
+ * that a caller can time the achievable HBM read rate that the decode kernels are measured
+ * against beside the specification.
+ *   buf    device memory, 16-byte aligned; bytes a positive multiple of 16.
+ *   sink   one device uint32 the kernel may write (to keep its loads alive).
+ *   grid   1 .. 65536.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_LAUNCH.
+ */
+int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

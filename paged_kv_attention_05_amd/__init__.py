@@ -29,7 +29,7 @@ ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR
 EXPORTS = ["paged_kv_write", "paged_kv_write_fp8", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
            "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
-           "paged_attn_set_timing", "paged_attn_timing_report"]
+           "paged_attn_set_timing", "paged_attn_timing_report", "paged_hbm_read_probe"]
 KINDS = ["kv_write", "plan", "prefill", "small", "merge"]
 
 _lib = None
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, P]
     lib.paged_kv_write_fp8.restype = ctypes.c_int
     lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I64, I32, P]
+    lib.paged_hbm_read_probe.restype = ctypes.c_int
+    lib.paged_hbm_read_probe.argtypes = [P, I64, P, I32, P]
     lib.paged_copy_blocks.restype = ctypes.c_int
     lib.paged_copy_blocks.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
     lib.paged_attention_workspace_bytes.restype = SZ
@@ -121,6 +123,13 @@ def set_debug_checks(enable: bool) -> None:
 def set_path(path: int) -> None:
     """0: automatic kernel choice; 1: vector-ALU tile kernel for every request."""
     load_library().paged_attn_set_path(int(path))
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:
+    """Read all of the device tensor buf once (measurement of the achievable HBM read rate)."""
+    lib = load_library()
+    _check(lib.paged_hbm_read_probe(_dptr(buf, "buf"), buf.numel() * buf.element_size(), _dptr(sink, "sink"),
+                                    int(grid), _stream(stream)))
 
 
 def set_timing(enable: bool) -> None:

@@ -448,4 +448,14 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   return PA_OK;
 }
 
+int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream) {
+  g_last_error.clear();
+  if (!buf || !sink) return fail(PA_ERR_NULL, "null pointer argument");
+  if (bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return fail(PA_ERR_SHAPE, "bytes must be a positive multiple of 16, buf 16-byte aligned");
+  if (grid < 1 || grid > 65536) return fail(PA_ERR_SHAPE, "grid must be in 1 .. 65536");
+  const hipError_t e = pa::launch_read_probe(buf, bytes, sink, grid, stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("read probe launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -195,6 +195,7 @@ hipError_t launch_small_valu(const Plan& p, const AttnArgs& a, void* ws, int32_t
 hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
 hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t s);
 // fp8 pools: stage the prefill requests' blocks as bf16 codes and scaled scales, then run the
 // prefill kernel on the staged copy
 hipError_t launch_stage_fp8(const Plan& p, const AttnArgs& a, float scale_abs_log2e, void* ws, hipStream_t s);

@@ -139,3 +139,15 @@ def test_graph_sizing():
     opts.graph_max_seq_len = -1
     assert lib.paged_attention_workspace_bytes_ex(3, 3, 32, 8, 128, 16, _host([0, 1, 2, 3]), None, 1,
                                                   ctypes.byref(opts)) == 0
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = pk.load_library()
+    sink = ctypes.c_void_p(0x2000)                 # never dereferenced: validation fails first
+    assert lib.paged_hbm_read_probe(None, 1024, sink, 64, None) == -1
+    assert lib.paged_hbm_read_probe(FAKE, 1024, None, 64, None) == -1
+    assert lib.paged_hbm_read_probe(FAKE, 1000, sink, 64, None) == -2                 # not a multiple of 16
+    assert lib.paged_hbm_read_probe(FAKE, 0, sink, 64, None) == -2
+    assert lib.paged_hbm_read_probe(ctypes.c_void_p(0x1008), 1024, sink, 64, None) == -2   # misaligned
+    assert lib.paged_hbm_read_probe(FAKE, 1024, sink, 0, None) == -2
+    assert lib.paged_hbm_read_probe(FAKE, 1024, sink, 70000, None) == -2

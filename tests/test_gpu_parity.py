@@ -681,3 +681,14 @@ def test_gpu_aliasing():
     b = workloads.small_batch([(0, 64), (64, 1), (100, 1), (64, 30)], dtype="bf16", num_heads=8, num_kv_heads=2,
                               head_dim=128, shared_prefix_blocks=4, seed=51)
     H.check_batch(b, label="aliased_prefix")
+
+
+def test_hbm_read_probe_runs():
+    """The measurement probe reads a buffer end to end (it writes its sink only for one
+    unlikely xor value) without an error."""
+    import paged_kv_attention_05_amd as pk
+    buf = torch.ones(16 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for grid in (1, 256, 4096):
+        pk.hbm_read_probe(buf, sink, grid)
+    torch.cuda.synchronize()
