@@ -83,6 +83,9 @@ def main() -> int:
                          "small tiles)")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the streaming read / copy probe of the achievable HBM bandwidth")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="launch only the warm-up and timed steps (no per-step spread, sub-calls or HBM "
+                         "probe), so that profiler counters see one set of launches per step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once: a plain copy "
                          "of known size whose HBM counters scale the kernels' counters")
@@ -176,7 +179,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    pk.set_timing(True)
+    # the timed steps, with no instrumentation in the stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -185,9 +188,15 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    eager_ms = ms_per_step
+    # per-kernel times: the same steps again, each library launch between HIP events on its
+    # stream (the events add a little time to these steps, not to the ones above)
+    pk.set_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     kern = pk.timing_report()
     pk.set_timing(False)
-    eager_ms = ms_per_step
     if args.graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -209,7 +218,8 @@ def main() -> int:
         ms_per_step = start.elapsed_time(end) / args.steps
         eprint(f"[bench] graph replays: {ms_per_step:.4f} ms/step (eager {eager_ms:.4f})")
     # per-step spread: the same steps again, each between its own events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [] if args.no_extras else \
+        [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1 in evs:
         e0.record()
         if args.graph:
@@ -219,7 +229,8 @@ def main() -> int:
         e1.record()
     torch.cuda.synchronize()
     per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    spread = {"median_ms": per_step[len(per_step) // 2], "min_ms": per_step[0], "max_ms": per_step[-1]}
+    spread = {"median_ms": per_step[len(per_step) // 2], "min_ms": per_step[0], "max_ms": per_step[-1]} \
+        if per_step else None
     kern_avg = {name: (tot / cnt if cnt else 0.0) for name, (tot, cnt) in kern.items()}
     eprint(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernels (avg ms): "
            + ", ".join(f"{n}={t:.4f}" for n, t in kern_avg.items() if t))
@@ -282,7 +293,7 @@ def main() -> int:
     # mixed batches: the decode-row and the prefill-row requests as sub-calls of their own
     # (attention only, over the pool the steps wrote)
     subcalls = None
-    if dec_ids and pf_ids and not args.graph:
+    if dec_ids and pf_ids and not args.graph and not args.no_extras:
         subcalls = {}
         for name, ids, w_sub in (("decode", dec_ids, w_dec), ("prefill", pf_ids, w_pf)):
             sub = _subset(torch, batch, ids, q, qsl.device)
@@ -306,7 +317,7 @@ def main() -> int:
                               "algorithmic_flops": w_sub["flops"], "gbps": w_sub["bytes"] / (ms * 1e-3) / 1e9,
                               "tflops": w_sub["flops"] / (ms * 1e-3) / 1e12}
 
-    hbm = None if args.no_hbm_probe else hbm_probe(torch, pk, dev)
+    hbm = None if (args.no_hbm_probe or args.no_extras) else hbm_probe(torch, pk, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
