@@ -82,7 +82,7 @@ def main() -> int:
                          "quantizing write and attends over the codes (bf16 batches; every request on the "
                          "small tiles)")
     ap.add_argument("--no-hbm-probe", action="store_true",
-                    help="skip the streaming read / copy probe of the achievable HBM bandwidth")
+                    help="skip the probes of the achievable HBM bandwidth and matrix-core rate")
     ap.add_argument("--no-extras", action="store_true",
                     help="launch only the warm-up and timed steps (no per-step spread, sub-calls or HBM "
                          "probe), so that profiler counters see one set of launches per step")
@@ -318,6 +318,7 @@ def main() -> int:
                               "tflops": w_sub["flops"] / (ms * 1e-3) / 1e12}
 
     hbm = None if (args.no_hbm_probe or args.no_extras) else hbm_probe(torch, pk, dev)
+    mfma = None if (args.no_hbm_probe or args.no_extras) else mfma_probe(torch, pk, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -347,6 +348,7 @@ def main() -> int:
         "step_spread": spread,
         "subcalls": subcalls,
         "hbm_probe": hbm,
+        "mfma_probe": mfma,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -450,6 +452,29 @@ def hbm_probe(torch, pk, dev, gib=4):
             "copy_gbps_read_plus_write": 2 * nbytes / (copy_ms * 1e-3) / 1e9,
             "how": "paged_hbm_read_probe (nontemporal 16-byte loads, 256 threads per workgroup) over 4 GiB, "
                    "and torch copy_ of 4 GiB; best of 5"}
+
+
+def mfma_probe(torch, pk, dev, iters=4096):
+    """Matrix-core rate the chip sustains beside the 2.5 PFLOP/s specification: the library's
+    probe of back-to-back bf16 32x32x16 products with no memory traffic (best over two grid
+    sizes, best of 5 each)."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rates = {}
+    for grid in (1024, 2048):
+        flops = pk.mfma_probe(iters, grid, sink)
+        times = []
+        for _ in range(5):
+            a.record()
+            pk.mfma_probe(iters, grid, sink)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        rates[grid] = flops / (min(times) * 1e-3) / 1e12
+    top = max(rates, key=rates.get)
+    return {"tflops": rates[top], "grid": top, "tflops_by_grid": {str(k): v for k, v in rates.items()},
+            "how": f"paged_mfma_probe: 512-thread workgroups, {iters} rounds of 8 independent "
+                   "32x32x16 bf16 products per wave, no memory traffic; best of 5"}
 
 
 def _cpu_model():

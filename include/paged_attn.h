@@ -271,6 +271,19 @@ int paged_attn_timing_report(double* total_ms, int32_t* count, int32_t n_kinds);
  */
 int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream);
 
+/*
+ * paged_mfma_probe (measurement only, not part of the attention path): `grid` workgroups of
+ * 512 threads each run `iters` rounds of eight independent 32x32x16 bf16 matrix products with
+ * no memory traffic, so that a caller can time the matrix-core rate the chip sustains under
+ * its clock and power limits, beside the 2.5 PFLOP/s specification the prefill kernel is
+ * measured against.
+ *   iters  1 .. 2^20;  grid 1 .. 65536.
+ *   sink   one device uint32 the kernel may write (to keep its products alive).
+ *   flops  optional host int64: receives the launch's floating-point operation count.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_LAUNCH.
+ */
+int paged_mfma_probe(int32_t iters, int32_t grid, uint32_t* sink, int64_t* flops, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR
 EXPORTS = ["paged_kv_write", "paged_kv_write_fp8", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
            "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
-           "paged_attn_set_timing", "paged_attn_timing_report", "paged_hbm_read_probe"]
+           "paged_attn_set_timing", "paged_attn_timing_report", "paged_hbm_read_probe", "paged_mfma_probe"]
 KINDS = ["kv_write", "plan", "prefill", "small", "merge"]
 
 _lib = None
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I64, I32, P]
     lib.paged_hbm_read_probe.restype = ctypes.c_int
     lib.paged_hbm_read_probe.argtypes = [P, I64, P, I32, P]
+    lib.paged_mfma_probe.restype = ctypes.c_int
+    lib.paged_mfma_probe.argtypes = [I32, I32, P, P, P]
     lib.paged_copy_blocks.restype = ctypes.c_int
     lib.paged_copy_blocks.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
     lib.paged_attention_workspace_bytes.restype = SZ
@@ -130,6 +132,15 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None
     lib = load_library()
     _check(lib.paged_hbm_read_probe(_dptr(buf, "buf"), buf.numel() * buf.element_size(), _dptr(sink, "sink"),
                                     int(grid), _stream(stream)))
+
+
+def mfma_probe(iters: int, grid: int, sink: torch.Tensor, stream=None) -> int:
+    """Run back-to-back bf16 matrix products (measurement of the sustained matrix-core rate);
+    returns the launch's floating-point operation count."""
+    lib = load_library()
+    flops = ctypes.c_int64(0)
+    _check(lib.paged_mfma_probe(int(iters), int(grid), _dptr(sink, "sink"), ctypes.byref(flops), _stream(stream)))
+    return flops.value
 
 
 def set_timing(enable: bool) -> None:

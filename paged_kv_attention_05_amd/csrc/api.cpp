@@ -458,4 +458,15 @@ int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t
   return PA_OK;
 }
 
+int paged_mfma_probe(int32_t iters, int32_t grid, uint32_t* sink, int64_t* flops, hipStream_t stream) {
+  g_last_error.clear();
+  if (!sink) return fail(PA_ERR_NULL, "null pointer argument");
+  if (iters < 1 || iters > (1 << 20)) return fail(PA_ERR_SHAPE, "iters must be in 1 .. 2^20");
+  if (grid < 1 || grid > 65536) return fail(PA_ERR_SHAPE, "grid must be in 1 .. 65536");
+  if (flops) *flops = pa::mfma_probe_flops(iters, grid);
+  const hipError_t e = pa::launch_mfma_probe(iters, sink, grid, stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("matrix probe launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // extern "C"

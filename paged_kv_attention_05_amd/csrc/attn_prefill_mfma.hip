@@ -79,6 +79,13 @@ __device__ __forceinline__ bf16x4 tr_read(uint32_t addr) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
   return __builtin_bit_cast(bf16x4, r);
 }
+// max of x over lanes l and l ^ 32, with one swap of the wave's halves (a vector-ALU
+// instruction: unlike a shuffle through the LDS crossbar, it does not queue behind the other
+// waves' LDS reads)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
 }
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[sh][r], s[sh][r + 1]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     const float mxs = mx * slx;                             // mx is finite or -inf, slx > 0
     // move the reference only when the row max grew by more than kLazy (or it is unset)
     if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {

@@ -151,3 +151,13 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.paged_hbm_read_probe(ctypes.c_void_p(0x1008), 1024, sink, 64, None) == -2   # misaligned
     assert lib.paged_hbm_read_probe(FAKE, 1024, sink, 0, None) == -2
     assert lib.paged_hbm_read_probe(FAKE, 1024, sink, 70000, None) == -2
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    lib = pk.load_library()
+    sink = ctypes.c_void_p(0x2000)                 # never dereferenced: validation fails first
+    assert lib.paged_mfma_probe(16, 64, None, None, None) == -1
+    assert lib.paged_mfma_probe(0, 64, sink, None, None) == -2
+    assert lib.paged_mfma_probe(1 << 21, 64, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 0, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 70000, sink, None, None) == -2

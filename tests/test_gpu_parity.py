@@ -683,6 +683,16 @@ def test_gpu_aliasing():
     H.check_batch(b, label="aliased_prefix")
 
 
+def test_mfma_probe_runs():
+    """The matrix-core probe runs and reports its launch's operation count: grid x 8 waves x
+    iters x 8 products x 2*32*32*16."""
+    import paged_kv_attention_05_amd as pk
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for iters, grid in ((1, 1), (64, 256), (16, 2048)):
+        assert pk.mfma_probe(iters, grid, sink) == grid * 8 * iters * 8 * 2 * 32 * 32 * 16
+    torch.cuda.synchronize()
+
+
 def test_hbm_read_probe_runs():
     """The measurement probe reads a buffer end to end (it writes its sink only for one
     unlikely xor value) without an error."""
