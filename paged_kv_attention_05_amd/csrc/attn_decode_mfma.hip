@@ -11,9 +11,9 @@
 // pool: a 16-token block of one KV head is 16 rows of D contiguous elements).
 //
 // Per wave and 16-key block (one pool block at block_size 16):
-//   S^T[key][col] = K[key][:] . Q[col][:]   mfma_f32_16x16x32_bf16, K straight from HBM into
-//                                           the A operand (lane: key = lane%16, 8 dims),
-//                                           Q^T held in registers as the B operand.
+//   S^T[key][col] = K[key][:] . Q[col][:]   mfma_f32_16x16x32_bf16, K as the A operand
+//                                           (lane: key = lane%16, 8 dims), Q^T held in
+//                                           registers as the B operand.
 //   online softmax per column               the lane owning column n keeps its running max;
 //                                           the 4 lane groups share it with two xor shuffles.
 //   O^T[d][col] += V^T[d][key] P^T[key][col] mfma_f32_16x16x16 bf16: P^T is the S^T
@@ -22,10 +22,10 @@
 //                                           LDS transpose read (ds_read_tr16_b64).
 // P is split into bf16 high and low parts (two products) so the probabilities keep ~16
 // bits: cheap here, since the path is bound by HBM, not by the matrix cores.
-// bf16 pools: K goes from HBM straight into registers and V straight into a per-wave LDS
-// buffer (gfx950 direct loads), two of each, so the next block is in flight while the
-// current one is computed.  fp8 pools: the codes of K and V go into two register sets
-// (ping-pong) and V is converted into the LDS buffer.  The block
+// bf16 pools: K and V go from HBM straight into two per-wave LDS buffers (gfx950 direct
+// loads of whole rows), are read into registers as soon as they land, and the next block's
+// loads are in flight while the current one is computed.  fp8 pools: the codes of K and V
+// go into two register sets (ping-pong) and V is converted into the LDS buffer.  The block
 // table is read with scalar loads (one entry per block), so no wait on a table entry drains
 // the vector loads in flight.  Keys past the split end are read from the last visible key
 // instead (finite data, masked), so no NaN from an unwritten slot enters.
@@ -64,6 +64,14 @@ __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
+// Chunk swizzle of a K row in LDS (chunk c of row r at slot c ^ kswz(r)): the A-operand
+// reads (16 rows x one chunk per lane group) hit 16 distinct 16-byte slots of the 256-byte
+// bank window.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
 __device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
@@ -98,7 +106,8 @@ template <int D, bool F8, int NC>
 __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
                                                                        int32_t total_idx, Partials part) {
   using C = DecodeCfg<D>;
-  // per wave: two V buffers; after the key loop the same bytes hold the per-wave output slabs
+  // per wave two block buffers (bf16: V and K; fp8: two V); after the key loop the same
+  // bytes hold the per-wave output slabs
   constexpr int kVBytes = 4 * 2 * C::VBUF;
   constexpr int kSlabBytes = 4 * kCols * D * 4;
   __shared__ __align__(1024) unsigned char smem[kVBytes > kSlabBytes ? kVBytes : kSlabBytes];
@@ -241,7 +250,14 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
     }
   };
 
-  auto compute = [&](int32_t lb, const bf16x8* kcur, const unsigned char* vb, const float* ks, const float* vs) {
+  // V^T operand of d tile dt (keys 4G + n/4 .. as the S^T accumulator holds them) from a
+  // wave's V buffer
+  auto vt_read = [&](const unsigned char* vb, int dt) -> bf16x4 {
+    const int r = 4 * G + (n >> 2);
+    const int chunk = 2 * dt + ((n & 3) >> 1);
+    return tr_read(vb + r * C::ROW + 16 * (chunk ^ vswz<D>(r)) + 8 * (n & 1));
+  };
+  auto compute = [&](int32_t lb, const bf16x8* kcur, auto&& vfrag, const float* ks, const float* vs) {
     const int32_t key0 = lb * kBlk + 4 * G;
     float alpha[NC];
     bf16x4 phi[NC], plo[NC];
@@ -285,9 +301,7 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
     // O^T = alpha * O^T + V^T P^T (one transpose read per d tile serves every tile)
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const int r = 4 * G + (n >> 2);
-      const int chunk = 2 * dt + ((n & 3) >> 1);
-      const bf16x4 vt = tr_read(vb + r * C::ROW + 16 * (chunk ^ vswz<D>(r)) + 8 * (n & 1));
+      const bf16x4 vt = vfrag(dt);
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         if (u >= ntile) break;
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
       float ks[4], vs[4];
       quad_bcast4(f.ks, ks);
       quad_bcast4(f.vs, vs);
-      compute(lb, kr, vb, ks, vs);
+      compute(lb, kr, [&](int dt) { return vt_read(vb, dt); }, ks, vs);
     };
     // this wave's blocks blk0, blk0 + 4, ... through two register sets: the loads of the next
     // block are issued before each block is computed (a third set measured slower).  They are
@@ -338,41 +352,38 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
       }
     }
   } else {
-    // K block into registers, V block straight into the wave's LDS buffer (gfx950 direct
-    // loads); two of each, ping-pong.  The explicit waits make block lb land before it is
-    // computed (the compiler adds a full wait for direct loads before the LDS reads).
-    auto load_direct = [&](int32_t lb, bf16x8* kr, unsigned char* dst) {
+    // K and V of a block go straight into this wave's two LDS buffers (gfx950 direct loads),
+    // every load instruction covering whole rows (RPI rows of D contiguous elements): a K
+    // read in the A-operand layout straight from HBM covers 16 rows x 64 bytes per
+    // instruction, which streams measurably slower than whole rows.  Each block is read
+    // out of LDS into registers (K operand, V^T operand) as soon as it has landed, and the
+    // next block's loads go out into the same buffers before the block is computed.
+    unsigned char* kbufw = vbuf0 + C::VBUF;
+    auto issue = [&](int32_t lb) {
       const int32_t tb = trow[lb];
-      const __bf16* kp = kc + slot(tb, lb, n) * row_elems + 8 * G;
-#pragma unroll
-      for (int kk = 0; kk < C::KC; ++kk) kr[kk] = *(const bf16x8*)(kp + 32 * kk);
 #pragma unroll
       for (int u = 0; u < C::VLOADS; ++u) {
         const int r = C::RPI * u + lane / C::CHUNKS;
-        const int chunk = (lane % C::CHUNKS) ^ vswz<D>(r);
-        load_lds16(vc + slot(tb, lb, r) * row_elems + 8 * chunk, dst + u * 1024);
+        const int64_t src = slot(tb, lb, r) * row_elems;
+        load_lds16(kc + src + 8 * ((lane % C::CHUNKS) ^ kswz<D>(r)), kbufw + u * 1024);
+        load_lds16(vc + src + 8 * ((lane % C::CHUNKS) ^ vswz<D>(r)), vbuf0 + u * 1024);
       }
     };
     const float ones[4] = {1.f, 1.f, 1.f, 1.f};
-    bf16x8 kA[C::KC], kB[C::KC];
-    if (blk0 < nblk_end) load_direct(blk0, kA, vbuf0);
-    for (int32_t lb = blk0; lb < nblk_end; lb += 8) {
-      const bool has1 = lb + 4 < nblk_end;
-      if (has1) {
-        load_direct(lb + 4, kB, vbuf0 + C::VBUF);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb landed
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      compute(lb, kA, vbuf0, ones, ones);
-      if (!has1) break;
-      if (lb + 8 < nblk_end) {
-        load_direct(lb + 8, kA, vbuf0);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::KC + C::VLOADS) : "memory");   // block lb+4 landed
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      compute(lb + 4, kB, vbuf0 + C::VBUF, ones, ones);
+    if (blk0 < nblk_end) issue(blk0);
+    for (int32_t lb = blk0; lb < nblk_end; lb += 4) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");            // block lb landed
+      bf16x8 kr[C::KC];
+      bf16x4 vt[C::DT];
+#pragma unroll
+      for (int kk = 0; kk < C::KC; ++kk)
+        kr[kk] = *(const bf16x8*)(kbufw + n * C::ROW + 16 * ((4 * kk + G) ^ kswz<D>(n)));
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) vt[dt] = vt_read(vbuf0, dt);
+      // the reads are done before the buffers are reloaded
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lb + 4 < nblk_end) issue(lb + 4);
+      compute(lb, kr, [&](int dt) { return vt[dt]; }, ones, ones);
     }
   }
 
