@@ -683,6 +683,30 @@ def test_gpu_aliasing():
     H.check_batch(b, label="aliased_prefix")
 
 
+def test_many_requests_cross_planner_chunks():
+    """More requests than the planner kernel takes in one chunk (1024): the per-request
+    offsets carry across chunks, and each chunk boundary sits between requests of different
+    kinds (decodes, verification rows, prefill chunks, zero-row and zero-length requests).
+    Both item lists are checked: the matrix-core kernels' and the vector kernel's."""
+    rng = np.random.default_rng(91)
+    specs = []
+    for r in range(2600):
+        if r in (1022, 1023, 2047, 2049):                   # prefill chunks at the chunk edges
+            specs.append((int(rng.integers(0, 300)), int(rng.integers(65, 200))))
+        elif r in (1024, 2048):
+            specs.append((int(rng.integers(1, 50)), 0))     # a request with no rows this step
+        elif r % 97 == 5:
+            specs.append((int(rng.integers(1, 400)), int(rng.integers(2, 10))))   # verification rows
+        elif r % 211 == 7:
+            specs.append((0, 1))                            # a first token
+        else:
+            specs.append((int(rng.integers(1, 300)), 1))    # decodes
+    b = workloads.small_batch(specs, dtype="bf16", num_heads=8, num_kv_heads=2, head_dim=128, seed=92)
+    assert b.num_reqs > 2048
+    H.check_batch(b, label="many_requests")
+    H.check_batch(b, path=1, label="many_requests_vector")
+
+
 def test_mfma_probe_runs():
     """The matrix-core probe runs and reports its launch's operation count: grid x 8 waves x
     iters x 8 products x 2*32*32*16."""
