@@ -133,6 +133,9 @@ EDGE = [
     # grouped small tiles with two head subsets per token (g = 32): groups cross tokens
     ("groups_two_head_subsets", [(70, 1), (5, 9), (300, 4), (2100, 2)], 32, 1, 64, 16, "bf16"),
     ("groups_g4_spec_splits", [(5000, 9), (2047, 5), (2049, 9), (100, 3)], 16, 4, 128, 16, "bf16"),
+    # g = 3 and g = 6 do not divide the prefill tile's 256 rows: long chunks take the small tiles
+    ("g3_chunks_on_small_tiles", [(300, 150), (10, 1), (0, 70), (2100, 33)], 12, 4, 128, 16, "bf16"),
+    ("g6_chunks_on_small_tiles", [(40, 120), (999, 1), (0, 17)], 12, 2, 128, 16, "bf16"),
 ]
 
 
