@@ -136,6 +136,9 @@ EDGE = [
     # g = 3 and g = 6 do not divide the prefill tile's 256 rows: long chunks take the small tiles
     ("g3_chunks_on_small_tiles", [(300, 150), (10, 1), (0, 70), (2100, 33)], 12, 4, 128, 16, "bf16"),
     ("g6_chunks_on_small_tiles", [(40, 120), (999, 1), (0, 17)], 12, 2, 128, 16, "bf16"),
+    # g = 4: 17 rows (68 columns) is the shortest chunk on the prefill tiles, 16 rows (64) the
+    # longest on the small tiles
+    ("prefill_threshold", [(100, 17), (5, 16), (0, 17), (3000, 16)], 32, 8, 128, 16, "bf16"),
 ]
 
 
