@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libpagedattn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "kv_write.hip", "block_copy.hip", "plan.hip", "attn_valu.hip", "attn_decode_mfma.hip",
            "attn_prefill_mfma.hip", "fp8_stage.hip", "hbm_probe.hip",
-           "mfma_probe.hip"]
+           "mfma_probe.hip", "v16_stage.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Per-file extra flags.  The prefill kernel never carries NaN through its arithmetic (keys
 # past the visible range are clamped to finite data, masked scores are -inf), so it runs

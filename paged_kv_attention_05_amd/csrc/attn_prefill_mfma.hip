@@ -13,7 +13,9 @@
 //
 // Data movement: each 64-key K and V tile goes from HBM straight into LDS with the gfx950
 // direct loads (global_load_lds_dwordx4, 16 bytes per lane, no register staging), into rings
-// of three tiles, so later tiles stream in while the current one is computed.  An LDS row is
+// of three tiles, so later tiles stream in while the current one is computed.  K comes from
+// the pool through the block table; V from an fp16 copy of the request's blocks made just
+// before (v16_stage.hip).  An LDS row is
 // one key's 256 bytes; its sixteen 16-byte chunks are stored XOR-swizzled (chunk c of row r
 // at slot c ^ f(r), f(r) = 4*(r%4) + (r/4)%4), which makes both the K reads (16 consecutive
 // rows, one chunk) and the V transpose reads (4 rows x 4 chunks) free of bank conflicts.
@@ -32,9 +34,9 @@
 // moved (and O rescaled) when a row's max grows by more than 8 (a factor 256), so rescaling
 // is rare; the sum uses the same reference, so the result is exact either way.
 //
-// Precision of PV: each V tile is converted in LDS from bf16 to fp16, which is exact for
-// |v| <= 65504, and P is rounded to nearest fp16 (p <= 256 here), with the row sum taken over
-// the same rounded values.  The output is then an exact convex combination of V rows whose
+// Precision of PV: V is converted from bf16 to fp16 (by the staging kernel), which is exact
+// for |v| <= 65504, and P is rounded to nearest fp16 (p <= 256 here), with the row sum taken
+// over the same rounded values.  The output is then an exact convex combination of V rows whose
 // weights are off by at most 2^-12 relative: a single bf16 P (2^-9) would use most of the
 // 2e-2 budget against ~10x outlier values.  An item that meets |v| > 65504 is redone by a
 // second kernel that keeps V in bf16 and carries P as a bf16 pair (truncated high part plus
@@ -122,10 +124,12 @@ __device__ __forceinline__ void load_lds4(const void* g, unsigned char* lds_wave
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds_wave_base)), "v"(g) : "memory");
 }
 
-// F16 = true: the fast kernel.  V tiles are converted to fp16 in LDS and P goes to the matrix
-// cores as fp16; a workgroup that meets a V value outside fp16's range (|v| > 65504) flags
-// its item (wide[lin] = 1) and its output is rewritten by the F16 = false kernel, launched
-// right after on the same stream, which keeps V in bf16 and carries P as a bf16 pair.
+// F16 = true: the fast kernel.  V comes already in fp16, from the copy that stage_v16
+// (v16_stage.hip) made of the request's blocks: request r's block j is staged block
+// req[r].stage + j, so V needs no table lookup.  P goes to the matrix cores as fp16.  An
+// item whose V leaves fp16's range (|v| > 65504) was flagged by the staging kernel
+// (wide[lin] = 1); its output is rewritten by the F16 = false kernel, launched right after
+// on the same stream, which reads V in bf16 from the pool and carries P as a bf16 pair.
 //
 // F8 = true (with F16 = false): fp8 pools.  The kernel reads the staged bf16 copy of the
 // request's codes (exact) through the staged block table, and the staged per-key scales:
@@ -140,10 +144,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   using C = PrefillCfg<D>;
   constexpr int ROWS = 32 * WAVES;
   constexpr int NT = 64 * WAVES;
-  // Rings of three tiles each: V as converted to fp16 (fast kernel only), V as loaded (bf16)
-  // and K.  The output staging reuses the first bytes.
+  // Rings of three tiles each: V (fp16 in the fast kernel, bf16 otherwise) and K.  The
+  // output staging reuses the first bytes.
   constexpr int NBUF = 3;
-  constexpr int V16_RING = 0, V_RING = F16 ? NBUF * C::TILE : 0, K_RING = V_RING + NBUF * C::TILE;
+  constexpr int V_RING = 0, K_RING = V_RING + NBUF * C::TILE;
   constexpr int SC_RING = K_RING + NBUF * C::TILE;            // F8: per tile 64 K then 64 V scales
   constexpr int SC_TILE = F8 ? 2 * kBK * 4 : 0;
   constexpr int OUT_BYTES = ROWS * C::ROW;
@@ -249,7 +253,30 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     }
   };
   auto issue_k = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(kc, j, bl, dst); };
-  auto issue_v = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(vc, j, bl, dst); };
+  // F16: the staged fp16 blocks of this request are consecutive: key k is in staged block
+  // stage0 + k/16 (stage0 = the request's first staged block minus the first block it holds)
+  const int32_t stage0 = F16 ? __builtin_amdgcn_readfirstlane(a.req[r_id].stage) - v16_first_block(a.window, t, L) : 0;
+  const uint16_t* v16 = F16 ? (const uint16_t*)a.v_staged + (int64_t)stage0 * blk_stride + (int64_t)hkv * D : nullptr;
+  auto issue_v = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
+    if constexpr (F16) {
+      j += t0;
+      if (j * kBK + kBK <= kend) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int bi = WAVES == 4 ? u : ((w >> 2) + (WAVES / 4) * u);
+          load_lds16(v16 + (int64_t)(4 * j + bi) * blk_stride, lane_off_b, dst + (w + WAVES * u) * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int32_t kg = min(j * kBK + 4 * (w + WAVES * u) + (lane >> 4), kend - 1);
+          load_lds16(v16 + (int64_t)kg * row_elems + 8 * chunk_sw, dst + (w + WAVES * u) * 1024);
+        }
+      }
+    } else {
+      issue(vc, j, bl, dst);
+    }
+  };
   // F8: the 64 K scales (wave 0) and V scales (wave 1) of tile j, one per lane, into the ring
   // slot at dst (K scales at +0, V scales at +256); staged layout [block][2][Hkv][16]
   auto issue_sc = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
@@ -284,7 +311,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   //   V (transpose reads):   key rows 16qc + 4h + i16/4 (+8), whose swizzle does not depend on qc
   uint32_t koff[C::KC], voff[C::DT][2];
   {
-    const uint32_t kring = lds_addr(smem + K_RING), vring = lds_addr(smem + (F16 ? V16_RING : V_RING));
+    const uint32_t kring = lds_addr(smem + K_RING), vring = lds_addr(smem + V_RING);
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
       koff[kk] = kring + n * C::ROW + 16 * ((2 * kk + h) ^ swz(n));
@@ -342,12 +369,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   //
   // Slots (barrier-separated): A runs M(i) in slot 2i and X(i) in slot 2i+1; B runs M(i) in
   // slot 2i+1 and X(i) in slot 2i+2.  Tile i lives in ring slot i % 3.  K tile i is read in
-  // slots 2i and 2i+1.  V tile i is converted to fp16 during M(i) (group A's half in slot 2i,
-  // group B's in slot 2i+1) and read in slots 2i+2 and 2i+3.  At the start of slot 2i every
-  // wave issues its share of V(i+1), then of K(i+2) (their ring slots were last read in slot
+  // slots 2i and 2i+1, V tile i in slots 2i+2 and 2i+3.  At the start of slot 2i every wave
+  // issues its share of V(i+1), then of K(i+2) (their ring slots were last read in slot
   // 2i-1).  The end of slot 2i+1 waits until only the K(i+2) loads may still be in flight
-  // (vmcnt counts in issue order): V(i+1) is converted in slots 2i+2 and 2i+3, K(i+2) gets
-  // four slots before slot 2i+4 reads it.
+  // (vmcnt counts in issue order): V(i+1) has two slots to spare before slot 2i+4 reads it,
+  // K(i+2) gets four slots before slot 2i+4 reads it.
   auto vbuf = [&](int b) { return smem + V_RING + b * C::TILE; };
   auto kbuf = [&](int b) { return smem + K_RING + b * C::TILE; };
   auto scbuf = [&](int b) { return smem + SC_RING + b * SC_TILE; };
@@ -384,44 +410,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     blK = fetch_blocks(i + 3);
   };
 
-  // V tile i to fp16 (ring slot P), two 16-byte chunks per thread.  bf16 values convert to
-  // fp16 exactly when |v| <= 65504 (fp16's largest finite value; values below 2^-14 become
-  // fp16 subnormals, off by at most 2^-25).  A value out of that range (or an infinity) marks
-  // the item for the bf16 kernel.  Each wave converts its threads' chunks during its own
-  // matrix phase of tile i: the LDS reads go out at the start of the phase and the arithmetic
-  // and stores run in four slices, one after each group of QK^T products, so they issue while
-  // the matrix core works.
-  bool wide_seen = false;                                    // wave-uniform
-  u32x4 cv_src[2], cv_dst[2];
-  float cv_amax = 0.f;
-  auto conv_begin = [&](auto par) {
-    constexpr int P = decltype(par)::value;
-    if constexpr (F16) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        cv_src[e] = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
-            lds_addr(smem + V_RING) + (uint32_t)(P * C::TILE + 16 * (tid + NT * e)));
-      cv_amax = 0.f;
-    }
-  };
-  auto conv_slice = [&](int g, auto par) {
-    constexpr int P = decltype(par)::value;
-    if constexpr (F16) {
-      const int e = g >> 1;
-#pragma unroll
-      for (int k = 2 * (g & 1); k < 2 * (g & 1) + 2; ++k) {
-        const float lo = __uint_as_float(cv_src[e][k] << 16), hi = __uint_as_float(cv_src[e][k] & 0xffff0000u);
-        cv_amax = fmaxf(cv_amax, fmaxf(fabsf(lo), fabsf(hi)));
-        const f16x2 hv = {(_Float16)lo, (_Float16)hi};
-        cv_dst[e][k] = __builtin_bit_cast(uint32_t, hv);
-      }
-      if (g & 1)
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(
-            lds_addr(smem + V16_RING) + (uint32_t)(P * C::TILE + 16 * (tid + NT * e))) = cv_dst[e];
-      if (g == 3) wide_seen |= __builtin_amdgcn_ballot_w64(cv_amax > 65504.f) != 0;
-    }
-  };
-
   f32x16 s[2];
   // P of the last vector phase: fp16 pairs (fast kernel), or the bf16 high parts with pl
   // holding the bf16 roundings of the remainders
@@ -437,7 +425,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   };
   auto phase_m = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
-    if (i < ntiles) conv_begin(par);
     // PV first: P(i-1) is dead before S(i) is produced, so the two share registers
     if (i >= 1) {
       // O^T += V^T P^T over the four 16-key chunks, per chunk one product per d tile (two in
@@ -471,7 +458,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (i < ntiles) qk(P, s, [&](int g) { conv_slice(g, par); });
+    if (i < ntiles) qk(P, s, [](int) {});
   };
   auto phase_x = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
@@ -603,9 +590,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     if (i + 2 <= ntiles) step(i + 2, P2{});
   }
   if (grp_a) bar();
-  if constexpr (F16) {
-    if (wide_seen && lane == 0) wide[lin] = 1;              // redo this item in bf16
-  }
 
   // normalise and stage the tile's output rows in LDS, then write them out coalesced
   lsum += lsum2;
@@ -659,9 +643,16 @@ hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipSt
                        (int32_t)p.n_pf, wide);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true, false>), grid, dim3(64 * kWaves), 0, s, a, items,
+  // bf16 pools: V to fp16 once (flagging out-of-range items), then the fast kernel on it
+  if (!p.v16) return hipErrorInvalidValue;
+  hipError_t e = launch_stage_v16(p, a, ws, s);
+  if (e != hipSuccess) return e;
+  AttnArgs av = a;
+  av.v_staged = (char*)ws + p.off_v16;
+  av.req = (const ReqOffsets*)((char*)ws + p.off_req);
+  hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true, false>), grid, dim3(64 * kWaves), 0, s, av, items,
                      (int32_t)p.n_pf, wide);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // items whose V left fp16's range (normally none: these workgroups exit at once)
   hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false, false>), grid, dim3(64 * kWaves), 0, s, a, items,

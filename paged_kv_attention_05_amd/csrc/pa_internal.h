@@ -56,13 +56,15 @@ struct Plan {
   int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
   int32_t window;                  // sliding window in tokens (0: none)
   int32_t f8;                      // 1: fp8 pools (prefill requests read a staged bf16 copy)
+  int32_t v16;                     // 1: bf16 pools whose prefill requests read V from a staged
+                                   //    fp16 copy
   int32_t stage_w;                 // f8: width of the staged block table (blocks per request)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed); n_small counts tile-splits
   int64_t n_g1, n_g3;              // matrix-core small kernels: single-tile and grouped items
   int64_t n_stage;                 // f8: staged blocks (all blocks of the prefill requests)
   // workspace layout (byte offsets)
   size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, off_g1, off_g3;
-  size_t off_f8_tab, off_f8_k, off_f8_v, off_f8_s, total_bytes;
+  size_t off_f8_tab, off_f8_k, off_f8_v, off_f8_s, off_v16, total_bytes;
 };
 
 struct alignas(16) SmallItem {
@@ -95,9 +97,21 @@ constexpr int kPrefillMinCols = 4 * kCols;
 __host__ __device__ __forceinline__ bool use_prefill_path(const Plan& p, int32_t t, int32_t L) {
   return p.pf_tokens > 0 && L > 0 && (int64_t)t * p.g > kPrefillMinCols;
 }
-// Staged blocks of request r with fp8 pools: every block of a prefill-path request.
+// First block of a prefill-path request that the fp16 V copy holds: under a sliding window
+// of w tokens its first row (at position L - t) sees keys from L - t - w + 1 on, and the
+// prefill tiles start at a multiple of 64 keys (four 16-key blocks) below that.
+__host__ __device__ __forceinline__ int32_t v16_first_block(int32_t window, int32_t t, int32_t L) {
+  if (window <= 0) return 0;
+  const int64_t k0 = (int64_t)L - t - window + 1;
+  return k0 <= 0 ? 0 : (int32_t)(4 * (k0 / 64));
+}
+// Staged blocks of request r: every block of a prefill-path request (fp8 pools), or the
+// blocks from v16_first_block on (the fp16 V copy of bf16 pools).
 __host__ __device__ __forceinline__ int32_t staged_blocks(const Plan& p, int32_t t, int32_t L) {
-  return (p.f8 && use_prefill_path(p, t, L)) ? (L + p.bs - 1) / p.bs : 0;
+  if (!use_prefill_path(p, t, L)) return 0;
+  if (p.f8) return (L + p.bs - 1) / p.bs;
+  if (p.v16) return (L + p.bs - 1) / p.bs - v16_first_block(p.window, t, L);
+  return 0;
 }
 // Keys one small tile of a request with context L can see: all L, or with a sliding window
 // of w tokens at most w + tile_tokens - 1 (the tile's rows are consecutive), plus up to 63
@@ -173,6 +187,11 @@ struct AttnArgs {
   // fp8 pools: float32 scales [num_slots, Hkv] of K and V (null: the pools hold q's dtype)
   const float* k_scale;
   const float* v_scale;
+  // bf16 pools with the staged V: the fp16 copy [staged block][16][Hkv][D] of the prefill
+  // requests' blocks (request r's block j at staged block req[r].stage + j - first, first =
+  // v16_first_block)
+  const void* v_staged;
+  const ReqOffsets* req;
 };
 
 struct Partials {
@@ -201,6 +220,9 @@ int64_t mfma_probe_flops(int32_t iters, int32_t grid);
 // fp8 pools: stage the prefill requests' blocks as bf16 codes and scaled scales, then run the
 // prefill kernel on the staged copy
 hipError_t launch_stage_fp8(const Plan& p, const AttnArgs& a, float scale_abs_log2e, void* ws, hipStream_t s);
+// bf16 pools: copy the prefill requests' V blocks to fp16 (flagging, for the bf16 prefill
+// kernel, the items whose V leaves fp16's range)
+hipError_t launch_stage_v16(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
 bool small_mfma_supported(int32_t D, int32_t bs);
 bool prefill_mfma_supported(int32_t D, int32_t bs, int32_t g);
 int32_t prefill_tile_tokens(int32_t g);
