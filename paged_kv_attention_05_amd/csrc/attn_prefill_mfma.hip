@@ -499,13 +499,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         }
       }
     }
-    float mx = kNegInf;
+    // two chains of three-operand maxima (one v_max3 per two scores)
+    float mxa = fmaxf(s[0][0], s[0][1]), mxb = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[sh][r], s[sh][r + 1]));
+    for (int r = 2; r < 16; r += 2) {
+      mxa = fmaxf(fmaxf(mxa, s[0][r]), s[0][r + 1]);
+      mxb = fmaxf(fmaxf(mxb, s[1][r]), s[1][r + 1]);
     }
-    mx = max_xor32(mx);
+    float mx = max_xor32(fmaxf(mxa, mxb));
     const float mxs = mx * slx;                             // mx is finite or -inf, slx > 0
     // move the reference only when the row max grew by more than kLazy (or it is unset)
     if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {
