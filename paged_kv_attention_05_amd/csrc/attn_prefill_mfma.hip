@@ -253,25 +253,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     }
   };
   auto issue_k = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(kc, j, bl, dst); };
-  // F16: the staged fp16 blocks of this request are consecutive: key k is in staged block
-  // stage0 + k/16 (stage0 = the request's first staged block minus the first block it holds)
+  // F16: V from the transposed fp16 copy ([staged block][Hkv][D][16 keys in kperm order]).
+  // The staged blocks of this request are consecutive, block k/16 of the request at staged
+  // block stage0 + k/16 (stage0 = its first staged block minus the first block it holds),
+  // and every tile's four blocks are staged (zeros past seq_len), so whole tiles are read.
+  // In LDS a V tile is four 4 KB blocks of 128 dim rows x 32 bytes; the two 16-byte halves
+  // of row d are swapped when bit 3 of d is set, which spreads a wave's operand reads (16
+  // consecutive dims, one half) over all banks.  Load instruction u of wave w fills the 1 KB
+  // piece I = w + WAVES*u: block I/4, dims 32(I%4) .. +31; lane l takes dim 32(I%4) + l/2,
+  // half (l%2) ^ (bit 3 of the dim).
+  static_assert(WAVES % 4 == 0, "a wave's V pieces share one dim range");
   const int32_t stage0 = F16 ? __builtin_amdgcn_readfirstlane(a.req[r_id].stage) - v16_first_block(a.window, t, L) : 0;
-  const uint16_t* v16 = F16 ? (const uint16_t*)a.v_staged + (int64_t)stage0 * blk_stride + (int64_t)hkv * D : nullptr;
+  const uint16_t* v16 = F16 ? (const uint16_t*)a.v_staged + (int64_t)stage0 * blk_stride + (int64_t)hkv * D * kBlk : nullptr;
+  const int vdim = 32 * (w & 3) + (lane >> 1);
+  const uint32_t v16_lane_off_b = (uint32_t)(vdim * 32 + 16 * ((lane & 1) ^ ((vdim >> 3) & 1)));
   auto issue_v = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
     if constexpr (F16) {
-      j += t0;
-      if (j * kBK + kBK <= kend) {
+      const uint16_t* tile = v16 + (int64_t)(4 * (j + t0)) * blk_stride;
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int bi = WAVES == 4 ? u : ((w >> 2) + (WAVES / 4) * u);
-          load_lds16(v16 + (int64_t)(4 * j + bi) * blk_stride, lane_off_b, dst + (w + WAVES * u) * 1024);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int32_t kg = min(j * kBK + 4 * (w + WAVES * u) + (lane >> 4), kend - 1);
-          load_lds16(v16 + (int64_t)kg * row_elems + 8 * chunk_sw, dst + (w + WAVES * u) * 1024);
-        }
+      for (int u = 0; u < UK; ++u) {
+        const int bi = (w + WAVES * u) >> 2;
+        load_lds16(tile + (int64_t)bi * blk_stride, v16_lane_off_b, dst + (w + WAVES * u) * 1024);
       }
     } else {
       issue(vc, j, bl, dst);
@@ -309,7 +311,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // (no extra address registers per ring slot).
   //   K (A operand of QK^T): key row 32*sh + n, chunk (2kk + h) ^ swz(n)   (swz(32+n) == swz(n))
   //   V (transpose reads):   key rows 16qc + 4h + i16/4 (+8), whose swizzle does not depend on qc
-  uint32_t koff[C::KC], voff[C::DT][2];
+  //   V^T, F16 (transposed copy): dim 32dt + n, half h ^ (bit 3 of n), one 16-byte read
+  uint32_t koff[C::KC], voff[C::DT][2], voff16[C::DT];
   {
     const uint32_t kring = lds_addr(smem + K_RING), vring = lds_addr(smem + V_RING);
 #pragma unroll
@@ -326,6 +329,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         voff[dt][hf] = vring + r * C::ROW + 16 * (chunk ^ swz(r)) + 8 * (i16 & 1);
         asm volatile("" : "+v"(voff[dt][hf]));
       }
+      voff16[dt] = vring + (32 * dt + n) * 32 + 16 * (h ^ ((n >> 3) & 1));
+      if constexpr (F16) asm volatile("" : "+v"(voff16[dt]));
     }
   }
   // F8: per-lane base of the scale reads (this lane's keys start at 4h in each 8-key run);
@@ -418,9 +423,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   auto read_v = [&](int b, int qc, u32x4* va) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const bf16x4 v0 = tr_read(voff[dt][0] + b * C::TILE + 16 * qc * C::ROW);
-      const bf16x4 v1 = tr_read(voff[dt][1] + b * C::TILE + 16 * qc * C::ROW);
-      va[dt] = __builtin_bit_cast(u32x4, bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      if constexpr (F16) {
+        // block qc of the tile (4 KB each): this lane's 8 keys of dim 32dt + n, one read
+        va[dt] = __builtin_bit_cast(u32x4, lds_read16(voff16[dt] + b * C::TILE + 4096 * qc));
+      } else {
+        const bf16x4 v0 = tr_read(voff[dt][0] + b * C::TILE + 16 * qc * C::ROW);
+        const bf16x4 v1 = tr_read(voff[dt][1] + b * C::TILE + 16 * qc * C::ROW);
+        va[dt] = __builtin_bit_cast(u32x4, bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      }
     }
   };
   auto phase_m = [&](int32_t i, auto par) {

@@ -105,12 +105,18 @@ __host__ __device__ __forceinline__ int32_t v16_first_block(int32_t window, int3
   const int64_t k0 = (int64_t)L - t - window + 1;
   return k0 <= 0 ? 0 : (int32_t)(4 * (k0 / 64));
 }
-// Staged blocks of request r: every block of a prefill-path request (fp8 pools), or the
-// blocks from v16_first_block on (the fp16 V copy of bf16 pools).
+// Order of the keys of a 16-key block in a row of the transposed fp16 V copy: position q
+// holds key kperm(q), bits 2 and 3 swapped (an involution).  It is the order in which the
+// prefill kernel's P^T fragments hold their keys, so that a lane's 8 keys of one dim are
+// one 16-byte read.
+__host__ __device__ __forceinline__ int kperm(int q) { return (q & 3) | ((q & 4) << 1) | ((q & 8) >> 1); }
+// Staged blocks of request r: every block of a prefill-path request (fp8 pools), or, for
+// the fp16 V copy of bf16 pools, the blocks of every 64-key tile from v16_first_block on
+// (the last tile's blocks past the request's end are staged as zeros).
 __host__ __device__ __forceinline__ int32_t staged_blocks(const Plan& p, int32_t t, int32_t L) {
   if (!use_prefill_path(p, t, L)) return 0;
   if (p.f8) return (L + p.bs - 1) / p.bs;
-  if (p.v16) return (L + p.bs - 1) / p.bs - v16_first_block(p.window, t, L);
+  if (p.v16) return 4 * ((L + 63) / 64) - v16_first_block(p.window, t, L);
   return 0;
 }
 // Keys one small tile of a request with context L can see: all L, or with a sliding window
@@ -187,9 +193,9 @@ struct AttnArgs {
   // fp8 pools: float32 scales [num_slots, Hkv] of K and V (null: the pools hold q's dtype)
   const float* k_scale;
   const float* v_scale;
-  // bf16 pools with the staged V: the fp16 copy [staged block][16][Hkv][D] of the prefill
-  // requests' blocks (request r's block j at staged block req[r].stage + j - first, first =
-  // v16_first_block)
+  // bf16 pools with the staged V: the transposed fp16 copy [staged block][Hkv][D][16] of the
+  // prefill requests' blocks (request r's block j at staged block req[r].stage + j - first,
+  // first = v16_first_block; within a row, position q holds key kperm(q))
   const void* v_staged;
   const ReqOffsets* req;
 };
