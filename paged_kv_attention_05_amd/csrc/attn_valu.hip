@@ -207,37 +207,62 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
 // Combine the splits of a small tile: M = max m_s, out = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s.
 // One thread per (column, dim) output; a workgroup takes 256 / D columns of one tile and KV
 // head (blockIdx.y picks the column group), so even a handful of long decodes spreads over
-// many compute units.
+// many compute units.  The kernel is a chain of dependent loads (item, then partials): the
+// item carries the tile's output row and row count, and the splits are read kMergeBatch at a
+// time, all loads of a batch in flight together, folded into a running maximum (the sums
+// rescaled when it grows).  A small batch's tiles have at most 8 splits: one round trip.
+constexpr int kMergeBatch = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void merge_splits(AttnArgs a, const MergeItem* __restrict__ items,
                                                     Partials part) {
   const int D = a.D;
   const int cols_per_wg = 256 / D;
-  if ((int32_t)(blockIdx.x / a.Hkv) >= __builtin_amdgcn_readfirstlane(a.totals[1])) return;
+  const int32_t idx = blockIdx.x / a.Hkv;
+  // the item is read together with the count: a workgroup past the count (a graph replayed
+  // with fewer items than its grid) reads a stale item inside the list and exits unused
+  const int32_t total = __builtin_amdgcn_readfirstlane(a.totals[1]);
+  const MergeItem it = items[idx];
+  asm volatile("" ::"s"(total), "s"(it.row0), "s"(it.ntok), "s"(it.hsub), "s"(it.first), "s"(it.nsplit),
+               "s"(a.g), "s"(a.tile_heads), "s"(a.H), "s"(part.m), "s"(part.l), "s"(part.acc), "s"(a.out));
+  if (idx >= total) return;
   const int hkv = blockIdx.x % a.Hkv;
-  const MergeItem it = items[blockIdx.x / a.Hkv];
   const int col = blockIdx.y * cols_per_wg + threadIdx.x / D;
   const int d = threadIdx.x % D;
   if (col >= kCols || threadIdx.x >= cols_per_wg * D) return;
-  const int32_t b = a.qsl[it.r], t = a.qsl[it.r + 1] - b;
-  const int32_t Tn = min(a.tile_tokens, t - it.tok0);
   const int32_t h0 = it.hsub * a.tile_heads;
   const int32_t HGn = min(a.tile_heads, a.g - h0);
   const int i = col / a.tile_heads, j = col - i * a.tile_heads;
-  if (i >= Tn || j >= HGn) return;
+  if (i >= it.ntok || j >= HGn) return;
   const int64_t base = ((int64_t)it.first * a.Hkv + hkv) * kCols + col;
   const int64_t step = (int64_t)a.Hkv * kCols;                  // next split of the same column
-  float M = kNegInf;
-  for (int s = 0; s < it.nsplit; ++s) M = fmaxf(M, part.m[base + s * step]);
-  float lt = 0.f, o = 0.f;
-  for (int s = 0; s < it.nsplit; ++s) {
-    const int64_t pi = base + s * step;
-    const float f = exp2f(part.m[pi] - M);
-    lt += f * part.l[pi];
-    o += f * part.acc[pi * D + d];
+  float M = kNegInf, lt = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < it.nsplit; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const bool in = s0 + k < it.nsplit;
+      const int64_t pi = base + (int64_t)(s0 + k) * step;
+      mv[k] = in ? part.m[pi] : kNegInf;
+      lv[k] = in ? part.l[pi] : 0.f;
+      av[k] = in ? part.acc[pi * D + d] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) Mn = fmaxf(Mn, mv[k]);
+    if (Mn == kNegInf) continue;                                 // no key seen yet
+    const float c = exp2f(M - Mn);                               // 0 while M is -inf
+    lt *= c;
+    o *= c;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float f = exp2f(mv[k] - Mn);
+      lt += f * lv[k];
+      o += f * av[k];
+    }
+    M = Mn;
   }
   T* out = (T*)a.out;
-  Elem<T>::store(out + ((int64_t)(b + it.tok0 + i) * a.H + hkv * a.g + h0 + j) * D + d, o / lt);
+  Elem<T>::store(out + ((int64_t)(it.row0 + i) * a.H + hkv * a.g + h0 + j) * D + d, o / lt);
 }
 
 template <typename T>

@@ -74,7 +74,9 @@ struct alignas(16) SmallItem {
 };
 struct alignas(16) MergeItem {
   int32_t r, tok0, hsub, first;
-  int32_t nsplit, pad0, pad1, pad2;
+  int32_t nsplit;
+  int32_t row0, ntok;      // the tile's first output row (query_start_loc[r] + tok0) and row count
+  int32_t pad0;
 };
 struct alignas(8) PfItem {
   int32_t r, tok0;

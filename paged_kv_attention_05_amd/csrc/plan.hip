@@ -6,7 +6,7 @@
 // per-request formula (request_counts), and this one-workgroup kernel writes the item lists
 // the attention kernels read: no host-to-device copy, so the whole step stays on the stream.
 //
-// Requests are processed in chunks of 1024: a block scan gives each request's offsets in
+// Requests are processed in chunks of 512: a block scan gives each request's offsets in
 // the three lists, then every thread expands items of the chunk, finding the owning request
 // by binary search over the chunk's offsets in LDS.
 #include "pa_internal.h"
@@ -14,10 +14,11 @@
 namespace pa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+// 512 threads: at 1024 the kernel's registers spill to scratch and it takes twice as long
+constexpr int kPlanThreads = 512;
 
 // Inclusive scans of K counts per thread over the workgroup at once: within each wave by
-// shuffles, then across the 16 waves through LDS (two barriers in all).  tot gets the
+// shuffles, then across the 8 waves through LDS (two barriers in all).  tot gets the
 // workgroup totals.
 template <int K>
 __device__ __forceinline__ void block_scan_multi(int32_t (&v)[K], int32_t (&tot)[K], int32_t* wave_tot) {
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
   __shared__ int32_t wave_tot[(kPlanThreads / 64) * 6];
   __shared__ int32_t o_small[kPlanThreads], o_merge[kPlanThreads], o_pf[kPlanThreads];
   __shared__ int32_t o_g1[kPlanThreads], o_g3[kPlanThreads];
-  __shared__ int32_t c_t[kPlanThreads], c_ns[kPlanThreads];
+  __shared__ int32_t c_t[kPlanThreads], c_ns[kPlanThreads], c_q0[kPlanThreads];
   __shared__ int32_t carry[6];
   const int tid = threadIdx.x;
   // the prefill kernel's per-workgroup "redo in bf16" flags start cleared every call
@@ -83,9 +84,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
   for (int base = 0; base < p.R; base += kPlanThreads) {
     const int r = base + tid;
     const int n = min(kPlanThreads, p.R - base);
-    int32_t ns_small = 0, ns_merge = 0, ns_pf = 0, nsplit = 1, t = 0, ns_stage = 0, n_g1 = 0, n_g3 = 0;
+    int32_t ns_small = 0, ns_merge = 0, ns_pf = 0, nsplit = 1, t = 0, ns_stage = 0, n_g1 = 0, n_g3 = 0, q0 = 0;
     if (r < p.R) {
-      t = qsl[r + 1] - qsl[r];
+      q0 = qsl[r];
+      t = qsl[r + 1] - q0;
       request_counts(p, t, seq_lens[r], &ns_small, &ns_merge, &ns_pf, &nsplit);
       ns_stage = staged_blocks(p, t, seq_lens[r]);
       small_groups(p, t, seq_lens[r], &n_g1, &n_g3);
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
     o_merge[tid] = cm + inc_m - ns_merge;
     o_pf[tid] = cp + inc_p - ns_pf;
     c_t[tid] = t;
+    c_q0[tid] = q0;
     c_ns[tid] = nsplit;
     if (r < p.R) req[r] = ReqOffsets{o_small[tid], o_merge[tid], o_pf[tid], nsplit, cg + inc_g - ns_stage,
                                      o_g1[tid], o_g3[tid], 0};
@@ -178,7 +181,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
       it.hsub = tile % p.hsubs;
       it.first = o_small[i] + tile * c_ns[i];
       it.nsplit = c_ns[i];
-      it.pad0 = it.pad1 = it.pad2 = 0;
+      it.row0 = c_q0[i] + it.tok0;
+      it.ntok = min(p.tile_tokens, c_t[i] - it.tok0);
+      it.pad0 = 0;
       merge[idx] = it;
     }
     for (int32_t idx = cp + tid; idx < cp + tot_p; idx += kPlanThreads) {

@@ -690,16 +690,16 @@ def test_gpu_aliasing():
 
 
 def test_many_requests_cross_planner_chunks():
-    """More requests than the planner kernel takes in one chunk (1024): the per-request
+    """More requests than the planner kernel takes in one chunk (512): the per-request
     offsets carry across chunks, and each chunk boundary sits between requests of different
     kinds (decodes, verification rows, prefill chunks, zero-row and zero-length requests).
     Both item lists are checked: the matrix-core kernels' and the vector kernel's."""
     rng = np.random.default_rng(91)
     specs = []
     for r in range(2600):
-        if r in (1022, 1023, 2047, 2049):                   # prefill chunks at the chunk edges
+        if r in (511, 1022, 1023, 1535, 2047, 2049):        # prefill chunks at the chunk edges
             specs.append((int(rng.integers(0, 300)), int(rng.integers(65, 200))))
-        elif r in (1024, 2048):
+        elif r in (512, 1024, 2048):
             specs.append((int(rng.integers(1, 50)), 0))     # a request with no rows this step
         elif r % 97 == 5:
             specs.append((int(rng.integers(1, 400)), int(rng.integers(2, 10))))   # verification rows
