@@ -161,3 +161,22 @@ def test_mfma_probe_rejects_bad_arguments():
     assert lib.paged_mfma_probe(1 << 21, 64, sink, None, None) == -2
     assert lib.paged_mfma_probe(16, 0, sink, None, None) == -2
     assert lib.paged_mfma_probe(16, 70000, sink, None, None) == -2
+
+
+def test_no_kernel_spills_registers():
+    """The build records the compiler's resource report for every kernel and refuses a
+    kernel that spills to scratch. The report covers each kernel family of the library, and
+    every kernel fits one compute unit's LDS (160 KiB)."""
+    from paged_kv_attention_05_amd import build as B
+    if not os.path.exists(B.RESOURCES):
+        B.build(verbose=False)
+    with open(B.RESOURCES) as f:
+        head, *rows = [line.rstrip("\n").split("\t") for line in f]
+    kernels = [dict(zip(head, r)) for r in rows]
+    names = " ".join(k["name"] for k in kernels)
+    for family in ("kv_copy16", "kv_quant_fp8", "copy_blocks16", "plan_kernel", "small_tile_valu",
+                   "merge_splits", "small_tile_mfma", "prefill_tile_mfma", "stage_fp8", "stage_v16"):
+        assert family in names, family
+    for k in kernels:
+        assert int(k["scratch"]) == 0 and int(k["vgpr_spill"]) == 0, k["name"]
+        assert int(k["lds"]) <= 160 * 1024, k["name"]
