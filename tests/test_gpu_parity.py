@@ -123,6 +123,9 @@ EDGE = [
     ("head_dim_96", [(77, 1), (3, 20)], 6, 2, 96, 16, "f32"),
     ("long_decode_many_splits", [(20000, 1), (9000, 1)], 8, 1, 128, 16, "bf16"),
     ("long_decode_f32", [(5000, 1)], 4, 2, 64, 16, "f32"),
+    # 9 and 17 key splits of 2048: the merge folds a full batch of 8 splits, then a partial one
+    ("merge_batches_9_17", [(16500, 1), (34000, 1), (4000, 3)], 8, 2, 128, 16, "bf16"),
+    ("merge_batches_f32", [(16500, 1), (2, 1)], 4, 1, 64, 16, "f32"),
     ("block_boundaries", [(15, 1), (16, 1), (31, 2), (32, 16), (47, 17)], 8, 2, 128, 16, "bf16"),
     ("chunk_ragged_tail", [(1000, 131), (0, 200)], 16, 4, 128, 16, "bf16"),
     ("prefill_g8_d64", [(500, 300), (0, 77), (2, 1)], 64, 8, 64, 16, "bf16"),
