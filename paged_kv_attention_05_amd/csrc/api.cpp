@@ -119,14 +119,13 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   pa::Plan p{};
   p.R = R; p.H = H; p.Hkv = Hkv; p.g = H / Hkv; p.D = D; p.bs = bs;
   p.window = window;
+  p.graph_max = graph_max;
   if (graph_max > 0)
     for (int32_t r = 0; r < R; ++r)
       if ((int64_t)(qsl[r + 1] - qsl[r]) * p.g > pa::kPrefillMinCols)
         return fail(PA_ERR_SHAPE, "graph_max_seq_len: request " + std::to_string(r) +
                                       " has more than 64 query columns (rows x group heads)");
-  if (p.g >= pa::kCols) { p.tile_heads = pa::kCols; p.tile_tokens = 1; }
-  else { p.tile_heads = p.g; p.tile_tokens = pa::kCols / p.g; }
-  p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
+  pa::set_tile_shape(p);
   const bool auto_path = g_path == 0;
   p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
                     ? pa::prefill_tile_tokens(p.g) : 0;

@@ -59,6 +59,8 @@ struct Plan {
   int32_t v16;                     // 1: bf16 pools whose prefill requests read V from a staged
                                    //    fp16 copy
   int32_t stage_w;                 // f8: width of the staged block table (blocks per request)
+  int32_t graph_max;               // > 0: the call is sized for every seq_len = graph_max (the
+                                   //      planner counts device lengths clamped to it)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed); n_small counts tile-splits
   int64_t n_g1, n_g3;              // matrix-core small kernels: single-tile and grouped items
   int64_t n_stage;                 // f8: staged blocks (all blocks of the prefill requests)
@@ -90,6 +92,20 @@ struct alignas(16) ReqOffsets {
 };
 // indices into the request offsets seen as int32 (the totals row req[R])
 constexpr int kTotalSmall = 0, kTotalMerge = 1, kTotalPf = 2, kTotalG1 = 5, kTotalG3 = 6;
+
+// Small-tile shape for a group of g query heads per KV head: 16 columns are 16/g tokens
+// times the g heads, or (g >= 16) one token times 16 of its heads, the group then being cut
+// into g/16 head subsets.
+__host__ __device__ __forceinline__ void set_tile_shape(Plan& p) {
+  if (p.g >= kCols) {
+    p.tile_heads = kCols;
+    p.tile_tokens = 1;
+  } else {
+    p.tile_heads = p.g;
+    p.tile_tokens = kCols / p.g;
+  }
+  p.hsubs = (p.g + p.tile_heads - 1) / p.tile_heads;
+}
 
 // Classification of request r, identical on host and device.  Up to four small tiles (64
 // query columns: decodes, speculative-verification rows, short chunks) stay on the small
@@ -162,6 +178,13 @@ __host__ __device__ __forceinline__ void request_counts(const Plan& p, int32_t t
 // kGroupTiles consecutive tiles and key split, which reads each K/V block once for the group.
 // (kGroupTiles tiles with bf16 pools; none with fp8 pools, whose kernel measured slower with
 // the registers of a second tile than re-reading the codes)
+//
+// The list a request goes to depends only on t, the plan and the window, never on L: a call
+// sized for a capacity (graph_max_seq_len) counts every request at L = capacity on the host,
+// and the planner kernel recounts it at its device length, which may be anything from 0 (a
+// padding row) up to the capacity.  Only the split count follows L, and it never decreases
+// as L grows, so the device's counts never exceed the host's.  Both kernels zero the rows of
+// a request with L = 0.
 constexpr int kGroupTiles = 3;
 __host__ __device__ __forceinline__ int32_t group_tiles(const Plan& p) { return p.f8 ? 1 : kGroupTiles; }
 __host__ __device__ __forceinline__ void small_groups(const Plan& p, int32_t t, int32_t L, int32_t* n1, int32_t* n3) {
@@ -170,7 +193,7 @@ __host__ __device__ __forceinline__ void small_groups(const Plan& p, int32_t t, 
   const int32_t tiles = ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
   const int32_t ns = small_nsplit(p, L);
   const int32_t gt = group_tiles(p);
-  if (tiles == 1 || gt == 1 || p.window > 0 || L <= 0) *n1 = tiles * ns;
+  if (tiles == 1 || gt == 1 || p.window > 0) *n1 = tiles * ns;
   else *n3 = ((tiles + gt - 1) / gt) * ns;
 }
 

@@ -88,9 +88,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
     if (r < p.R) {
       q0 = qsl[r];
       t = qsl[r + 1] - q0;
-      request_counts(p, t, seq_lens[r], &ns_small, &ns_merge, &ns_pf, &nsplit);
-      ns_stage = staged_blocks(p, t, seq_lens[r]);
-      small_groups(p, t, seq_lens[r], &n_g1, &n_g3);
+      // a call sized for a capacity: lengths past it (a caller's precondition violation)
+      // are counted at the capacity, so the lists never outgrow what the host sized
+      const int32_t L = p.graph_max > 0 ? min(seq_lens[r], p.graph_max) : seq_lens[r];
+      request_counts(p, t, L, &ns_small, &ns_merge, &ns_pf, &nsplit);
+      ns_stage = staged_blocks(p, t, L);
+      small_groups(p, t, L, &n_g1, &n_g3);
     }
     const int32_t cs = carry[0], cm = carry[1], cp = carry[2], cg = carry[3], c1 = carry[4], c3 = carry[5];
     int32_t inc[6] = {ns_small, ns_merge, ns_pf, ns_stage, n_g1, n_g3}, tot[6];
