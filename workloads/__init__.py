@@ -29,6 +29,7 @@ import math
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -75,7 +76,7 @@ class Batch:
 
     @property
     def num_tokens(self) -> int:
-        return int(self.q.shape[0])
+        return int(self.query_start_loc_host[-1])
 
     @property
     def num_reqs(self) -> int:
@@ -92,40 +93,53 @@ def slot_of(table: Sequence[int], position: int, block_size: int) -> int:
 
 
 def batch_metadata(requests: Sequence[Request], block_size: int, pad_to: Optional[int] = None):
-    """Positions, slots, query_start_loc, seq_lens and the zero-padded table, laid out the way
-    the pages' build_batch does (padding rows: slot -1, seq_len 0, one query row)."""
-    positions, slots, starts, lengths, tables = [], [], [0], [], []
-    for req in requests:
-        c, n = req.computed, req.new
-        if len(req.blocks) * block_size < c + n:
-            raise ValueError("request has too few blocks for its sequence")
-        positions.extend(range(c, c + n))
-        slots.extend(slot_of(req.blocks, p, block_size) for p in range(c, c + n))
-        starts.append(starts[-1] + n)
-        lengths.append(c + n)
-        tables.append(list(req.blocks))
-    if pad_to is not None:
-        for _ in range(pad_to - len(lengths)):
-            positions.append(0)
-            slots.append(-1)
-            starts.append(starts[-1] + 1)
-            lengths.append(0)
-            tables.append([])
-    width = max(1, max(len(t) for t in tables))
-    table = torch.zeros((len(tables), width), dtype=torch.int32)
-    for r, t in enumerate(tables):
-        if t:
-            table[r, :len(t)] = torch.tensor(t, dtype=torch.int32)
+    """The BatchMeta arrays of a flattened batch ("Flattened ragged batches"): per-row
+    positions and pool slots, query_start_loc, seq_lens and a zero-padded block table.
+    pad_to > len(requests) appends padding requests of one row each, with seq_len 0, no
+    blocks and slot -1 (the scratch slot).
+
+    Built from per-request arrays: query_start_loc is the running sum of the row counts, each
+    row finds its request by a search over it, and its position and slot follow from the
+    request's first computed position and its table row."""
+    real = len(requests)
+    n_pad = max(0, (pad_to or 0) - real)
+    computed = np.array([r.computed for r in requests] + [0] * n_pad, dtype=np.int64)
+    rows = np.array([r.new for r in requests] + [1] * n_pad, dtype=np.int64)
+    ctx = computed + rows
+    ctx[real:] = 0                                        # padding: nothing to attend to
+    counts = np.array([len(r.blocks) for r in requests] + [0] * n_pad, dtype=np.int64)
+    short = np.nonzero(counts[:real] * block_size < ctx[:real])[0]
+    if len(short):
+        raise ValueError(f"request {int(short[0])} has too few blocks for its sequence")
+    qsl = np.zeros(real + n_pad + 1, dtype=np.int64)
+    np.cumsum(rows, out=qsl[1:])
+    # block table: every request's ids laid out along its row, zeros after them
+    table = np.zeros((real + n_pad, max(1, int(counts.max(initial=0)))), dtype=np.int32)
+    if counts.sum():
+        ids = np.concatenate([np.asarray(r.blocks, dtype=np.int64) for r in requests])
+        owner = np.repeat(np.arange(real + n_pad), counts)
+        col = np.arange(len(ids)) - np.repeat(np.cumsum(counts) - counts, counts)
+        table[owner, col] = ids
+    # rows: owning request, position, slot (padding rows: position 0, slot -1)
+    n = int(qsl[-1])
+    owner = np.searchsorted(qsl, np.arange(n), side="right") - 1
+    pos = computed[owner] + (np.arange(n) - qsl[owner])
+    pad_row = owner >= real
+    pos[pad_row] = 0
+    slot = table[owner, pos // block_size].astype(np.int64) * block_size + pos % block_size
+    slot[pad_row] = -1
+    qsl_list = [int(x) for x in qsl]
+    lens_list = [int(x) for x in ctx]
     return dict(
-        positions=torch.tensor(positions, dtype=torch.int64),
-        slot_mapping=torch.tensor(slots, dtype=torch.int64),
-        query_start_loc=torch.tensor(starts, dtype=torch.int32),
-        seq_lens=torch.tensor(lengths, dtype=torch.int32),
-        block_table=table,
-        query_start_loc_host=list(starts),
-        seq_lens_host=list(lengths),
-        max_query_len=max(b - a for a, b in zip(starts, starts[1:])),
-        max_seq_len=max(lengths),
+        positions=torch.from_numpy(pos.astype(np.int64)),
+        slot_mapping=torch.from_numpy(slot.astype(np.int64)),
+        query_start_loc=torch.tensor(qsl_list, dtype=torch.int32),
+        seq_lens=torch.tensor(lens_list, dtype=torch.int32),
+        block_table=torch.from_numpy(table),
+        query_start_loc_host=qsl_list,
+        seq_lens_host=lens_list,
+        max_query_len=int(rows.max(initial=0)),
+        max_seq_len=int(ctx.max(initial=0)),
     )
 
 
@@ -158,11 +172,19 @@ def assign_blocks(gen: torch.Generator, requests: Sequence[Request], num_blocks:
 def make_batch(name: str, requests: List[Request], *, dtype: str, num_heads: int, num_kv_heads: int,
                head_dim: int, block_size: int, num_blocks: int, gen: torch.Generator,
                poison: bool = True, outlier_p: float = 0.0, pad_to: Optional[int] = None,
-               scale: Optional[float] = None, description: str = "") -> Batch:
-    """Draw the pool contents and the new q, k, v for requests whose blocks are assigned."""
+               scale: Optional[float] = None, description: str = "", values: bool = True) -> Batch:
+    """Draw the pool contents and the new q, k, v for requests whose blocks are assigned.
+    values=False lays out the metadata only: the data tensors are then empty (for checks of
+    the batch's shape and indexing that need no values)."""
     meta = batch_metadata(requests, block_size, pad_to)
     hkv, d, bs = num_kv_heads, head_dim, block_size
     n = len(meta["positions"])
+    if not values:
+        e = torch.empty(0)
+        return Batch(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=hkv, head_dim=d,
+                     block_size=bs, num_blocks=num_blocks, requests=list(requests),
+                     scale=(1.0 / math.sqrt(d)) if scale is None else scale,
+                     q=e, k=e, v=e, k_cache=e, v_cache=e, description=description, **meta)
     written = set(s for s in meta["slot_mapping"].tolist() if s >= 0)
     context = set()
     for req in requests:
@@ -191,7 +213,7 @@ def make_batch(name: str, requests: List[Request], *, dtype: str, num_heads: int
 # length distributions stand in for the pages' lognormal request mix and shared prompts.
 # ----------------------------------------------------------------------------------------
 
-def worked_batch(poison: bool = True, seed: int = 1) -> Batch:
+def worked_batch(poison: bool = True, seed: int = 1, values: bool = True) -> Batch:
     """The 9-token batch of "Flattened ragged batches": a chunk of 3 at positions 6-8,
     decodes at 41 and 9, and a new request of 4 tokens.  fp32, 8/4 heads, D=48, bs=16,
     a 64-block pool whose tables are the first ids of a random permutation."""
@@ -199,11 +221,11 @@ def worked_batch(poison: bool = True, seed: int = 1) -> Batch:
     reqs = [Request(6, 3), Request(41, 1), Request(9, 1), Request(0, 4)]
     assign_blocks(gen, reqs, 64, 16)
     return make_batch("worked_batch", reqs, dtype="f32", num_heads=8, num_kv_heads=4, head_dim=48,
-                      block_size=16, num_blocks=64, gen=gen, poison=poison,
+                      block_size=16, num_blocks=64, gen=gen, poison=poison, values=values,
                       description="9 tokens / 4 requests, fp32, H=8 Hkv=4 D=48 bs=16, 64-block pool")
 
 
-def mixed_step(dtype: str = "f32", poison: bool = True, seed: int = 2) -> Batch:
+def mixed_step(dtype: str = "f32", poison: bool = True, seed: int = 2, values: bool = True) -> Batch:
     """48 requests: seq_len ~ lognormal(4.463, 0.701) clipped to [17, 443]; the first 8 are
     prefill chunks of min(64, seq_len) tokens, the other 40 decode one token.  A budget of
     512 tokens is applied decodes first, then chunks in order, each capped by what is left."""
@@ -227,12 +249,12 @@ def mixed_step(dtype: str = "f32", poison: bool = True, seed: int = 2) -> Batch:
     nb = math.ceil(1.2 * need)
     assign_blocks(gen, reqs, nb, 16)
     return make_batch(f"mixed_step_{dtype}", reqs, dtype=dtype, num_heads=8, num_kv_heads=4, head_dim=48,
-                      block_size=16, num_blocks=nb, gen=gen, poison=poison,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, values=values,
                       description="48 requests (40 decodes + 8 chunks <= 64), budget 512, H=8 Hkv=4 D=48")
 
 
 def decode_only(poison: bool = True, seed: int = 3, num_reqs: int = 256, min_len: int = 512,
-                max_len: int = 8192) -> Batch:
+                max_len: int = 8192, values: bool = True) -> Batch:
     """256 single-token decodes, seq_len ~ U{512..8192}, bf16, 32/8 heads, D=128, bs=16,
     pool 1.2x the blocks needed, tables scattered by a random permutation."""
     gen = torch.Generator().manual_seed(seed)
@@ -242,11 +264,11 @@ def decode_only(poison: bool = True, seed: int = 3, num_reqs: int = 256, min_len
     nb = math.ceil(1.2 * need)
     assign_blocks(gen, reqs, nb, 16)
     return make_batch("decode_only", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, num_blocks=nb, gen=gen, poison=poison,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, values=values,
                       description=f"{num_reqs} decodes, seq_len U{{{min_len}..{max_len}}}, bf16 H=32 Hkv=8 D=128")
 
 
-def shared_prefix(poison: bool = True, seed: int = 4) -> Batch:
+def shared_prefix(poison: bool = True, seed: int = 4, values: bool = True) -> Batch:
     """64 requests whose tables start with the same 16 blocks (a 256-token shared prefix):
     60 decodes with seq_len ~ U{300..4000} and 4 prefill chunks of 2048 tokens at
     num_computed_tokens (0, 2048, 4096, 2048).  Budget 8192, decodes first, then the chunks
@@ -264,23 +286,23 @@ def shared_prefix(poison: bool = True, seed: int = 4) -> Batch:
     nb = math.ceil(1.2 * need)
     assign_blocks(gen, reqs, nb, 16, shared_prefix_blocks=16)
     return make_batch("shared_prefix", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, num_blocks=nb, gen=gen, poison=poison,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, values=values,
                       description="60 decodes + 4 chunks (2048,2048,2048,1988), 256-token shared prefix")
 
 
-def long_context(poison: bool = True, seed: int = 5) -> Batch:
+def long_context(poison: bool = True, seed: int = 5, values: bool = True) -> Batch:
     """16 decodes at seq_len 32768 plus one prefill chunk of 4096 tokens at position 28672,
     bf16, 64/8 heads, D=128, a 40000-block pool, every value N(0,1) with 1% scaled by 10."""
     gen = torch.Generator().manual_seed(seed)
     reqs = [Request(32767, 1) for _ in range(16)] + [Request(28672, 4096)]
     assign_blocks(gen, reqs, 40000, 16)
     return make_batch("long_context", reqs, dtype="bf16", num_heads=64, num_kv_heads=8, head_dim=128,
-                      block_size=16, num_blocks=40000, gen=gen, poison=poison, outlier_p=0.01,
+                      block_size=16, num_blocks=40000, gen=gen, poison=poison, values=values, outlier_p=0.01,
                       description="16 decodes at 32768 + 1 chunk of 4096 at 28672, H=64 Hkv=8 D=128")
 
 
 def spec_verify(poison: bool = True, seed: int = 6, num_reqs: int = 128, min_len: int = 512,
-                max_len: int = 8192) -> Batch:
+                max_len: int = 8192, values: bool = True) -> Batch:
     """Speculative verification: every request scores 1 + k new rows (its last accepted
     token and k draft tokens), k cycling over 1, 2, 4, 8, at seq_len ~ U{512..8192} that
     includes those rows; bf16, 32/8 heads, D=128, bs=16, pool 1.2x the blocks needed.
@@ -293,12 +315,12 @@ def spec_verify(poison: bool = True, seed: int = 6, num_reqs: int = 128, min_len
     nb = math.ceil(1.2 * need)
     assign_blocks(gen, reqs, nb, 16)
     return make_batch("spec_verify", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, num_blocks=nb, gen=gen, poison=poison,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, values=values,
                       description=f"{num_reqs} verifications of 1+k rows, k in (1,2,4,8), seq_len "
                                   f"U{{{min_len}..{max_len}}}, bf16 H=32 Hkv=8 D=128")
 
 
-def small_decode(poison: bool = True, seed: int = 7) -> Batch:
+def small_decode(poison: bool = True, seed: int = 7, values: bool = True) -> Batch:
     """A decode batch of 13 requests padded to 16 rows (pad_to of "Flattened ragged
     batches": three rows with slot -1 and seq_len 0, the shape a captured graph serves),
     seq_len ~ U{256..2048}, bf16, 32/8 heads, D=128, bs=16, pool 1.2x the blocks needed."""
@@ -309,14 +331,14 @@ def small_decode(poison: bool = True, seed: int = 7) -> Batch:
     nb = math.ceil(1.2 * need)
     assign_blocks(gen, reqs, nb, 16)
     return make_batch("small_decode", reqs, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, num_blocks=nb, gen=gen, poison=poison, pad_to=16,
+                      block_size=16, num_blocks=nb, gen=gen, poison=poison, values=values, pad_to=16,
                       description="13 decodes padded to 16 rows, seq_len U{256..2048}, bf16 H=32 Hkv=8 D=128")
 
 
 CONFIGS = {
     "worked_batch": worked_batch,
-    "mixed_step_f32": lambda poison=True: mixed_step("f32", poison),
-    "mixed_step_bf16": lambda poison=True: mixed_step("bf16", poison),
+    "mixed_step_f32": lambda poison=True, values=True: mixed_step("f32", poison, values=values),
+    "mixed_step_bf16": lambda poison=True, values=True: mixed_step("bf16", poison, values=values),
     "decode_only": decode_only,
     "shared_prefix": shared_prefix,
     "long_context": long_context,
@@ -329,7 +351,7 @@ def small_batch(specs: Sequence[Tuple[int, int]], *, dtype: str = "f32", num_hea
                 num_kv_heads: int = 2, head_dim: int = 16, block_size: int = 16,
                 num_blocks: Optional[int] = None, seed: int = 0, poison: bool = True,
                 shared_prefix_blocks: int = 0, outlier_p: float = 0.0,
-                pad_to: Optional[int] = None) -> Batch:
+                pad_to: Optional[int] = None, values: bool = True) -> Batch:
     """A batch of requests given as (computed, new) pairs, for tests."""
     gen = torch.Generator().manual_seed(seed)
     reqs = [Request(c, t) for c, t in specs]
@@ -337,5 +359,5 @@ def small_batch(specs: Sequence[Tuple[int, int]], *, dtype: str = "f32", num_hea
     nb = num_blocks if num_blocks is not None else max(1, math.ceil(1.5 * need) + 2)
     assign_blocks(gen, reqs, nb, block_size, shared_prefix_blocks)
     return make_batch("small", reqs, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
-                      head_dim=head_dim, block_size=block_size, num_blocks=nb, gen=gen, poison=poison,
+                      head_dim=head_dim, block_size=block_size, num_blocks=nb, gen=gen, poison=poison, values=values,
                       outlier_p=outlier_p, pad_to=pad_to)
