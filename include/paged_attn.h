@@ -11,7 +11,9 @@
  *   - All tensors are dense, row-major, on the current HIP device; pointers are device
  *     pointers unless the name ends in _host.  The caller allocates and owns every buffer,
  *     including the workspace; the library never allocates device memory, never frees, and
- *     keeps no pointer after returning.
+ *     keeps no pointer after returning.  The one exception is the fixed scratch array of
+ *     paged_attention_varlen_noalloc, a static device array each GPU holds from the
+ *     library's load until the process ends.
  *   - dtype codes: PA_DTYPE_F32 (IEEE float32) and PA_DTYPE_BF16 (bfloat16).
  *   - Work is enqueued on `stream` and is asynchronous; nothing synchronises the device.
  *     The KV write of a step must be enqueued before the attention that reads it, on the
@@ -225,6 +227,36 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
                               const int32_t* seq_lens_host, int32_t max_query_len,
                               int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                               int32_t dtype, hipStream_t stream, const pa_attention_options* options);
+
+/*
+ * paged_attention_varlen_noalloc: paged_attention_varlen_ex without a workspace argument, for
+ * callers that cannot allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments (minus workspace
+ * and workspace_bytes), same contract, same kernels and the same results bit for bit.
+ *
+ * The workspace is a fixed scratch array of PA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU, held from the library's load until the process ends; its device
+ * address is looked up once per device on the first call there.  A batch whose workspace
+ * (paged_attention_workspace_bytes_ex for the same options) exceeds that size is refused
+ * with PA_ERR_WORKSPACE before anything is enqueued.  The call allocates no device memory
+ * and calls no hipMalloc, hipFree or hipMemset.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last call's
+ * contents: each call rewrites everything it reads (the planner writes the work lists and
+ * clears the per-item flags before any kernel reads them), so nothing needs clearing
+ * between calls.  Calls that may overlap on one GPU (different streams without ordering,
+ * or different threads) race on the array: order them on one stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_attention_varlen_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int32_t* block_table, int32_t block_size, float scale, void* out,
+                                   int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                                   int64_t num_slots, const int32_t* query_start_loc_host,
+                                   const int32_t* seq_lens_host, int32_t max_query_len,
+                                   int32_t max_seq_len, int32_t dtype, hipStream_t stream,
+                                   const pa_attention_options* options);
 
 /*
  * paged_attn_set_debug_checks: when enable != 0, later calls on this thread also copy

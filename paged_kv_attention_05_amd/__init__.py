@@ -24,10 +24,11 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 PA_DTYPE_FP8_E4M3 = 2
+NOALLOC_SCRATCH_BYTES = 64 << 20     # PA_NOALLOC_SCRATCH_BYTES of the C ABI
 ERRORS = {-1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE", -4: "PA_ERR_METADATA",
           -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_RANGE"}
 EXPORTS = ["paged_kv_write", "paged_kv_write_fp8", "paged_copy_blocks", "paged_attention_varlen", "paged_attention_workspace_bytes",
-           "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex",
+           "paged_attention_varlen_ex", "paged_attention_workspace_bytes_ex", "paged_attention_varlen_noalloc",
            "paged_attn_last_error", "paged_attn_set_debug_checks", "paged_attn_set_path",
            "paged_attn_set_timing", "paged_attn_timing_report", "paged_hbm_read_probe", "paged_mfma_probe"]
 KINDS = ["kv_write", "plan", "prefill", "small", "merge"]
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attention_varlen_ex.restype = ctypes.c_int
     lib.paged_attention_varlen_ex.argtypes = [P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I64, I32, I32,
                                               I32, I32, I64, P, P, I32, I32, P, SZ, I32, P, OPT]
+    lib.paged_attention_varlen_noalloc.restype = ctypes.c_int
+    lib.paged_attention_varlen_noalloc.argtypes = [P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I64, I32, I32,
+                                                   I32, I32, I64, P, P, I32, I32, I32, P, OPT]
     lib.paged_attn_last_error.restype = ctypes.c_char_p
     lib.paged_attn_last_error.argtypes = []
     lib.paged_attn_set_debug_checks.restype = None
@@ -253,14 +257,16 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            max_query_len: int = 0, max_seq_len: int = 0,
                            workspace: Optional[torch.Tensor] = None, stream=None,
                            sliding_window: int = 0, graph_max_seq_len: int = 0,
-                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None
-                           ) -> torch.Tensor:
+                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                           noalloc: bool = False) -> torch.Tensor:
     """Causal attention of the flattened batch over the pool; returns out [N, H, D].
     sliding_window > 0 limits the row at position p to keys p - sliding_window + 1 .. p.
     graph_max_seq_len > 0 sizes the launches for any device seq_lens up to it (for a call
     captured in a graph and replayed as the contexts grow); seq_lens_host may be None.
     With k_scale / v_scale ([NB+1, bs, Hkv] float32) the caches are fp8 E4M3 pools (uint8
-    codes written by paged_kv_write_fp8) and q / out are bf16."""
+    codes written by paged_kv_write_fp8) and q / out are bf16.
+    noalloc=True calls paged_attention_varlen_noalloc: the library's fixed per-GPU scratch
+    array serves as the workspace (workspace must then be None; out must be given)."""
     lib = load_library()
     n, h, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[1] != block_size or k_cache.shape[3] != d:
@@ -279,6 +285,8 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens), ("block_table", block_table)):
         if t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
+    if noalloc and (workspace is not None or out is None):
+        raise ValueError("noalloc: pass out and no workspace")
     if out is None:
         out = torch.empty_like(q)
     hkv = k_cache.shape[2]
@@ -286,11 +294,18 @@ def paged_attention_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     qh = _host_i32(query_start_loc_host)
     sh = _host_i32(seq_lens_host) if seq_lens_host is not None else None
     ref, _keep = _options(sliding_window, graph_max_seq_len, k_scale, v_scale)
+    stride = block_table.shape[1] if block_table.dim() == 2 else 0
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    if noalloc:
+        _check(lib.paged_attention_varlen_noalloc(
+            _dptr(q, "q"), _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"),
+            _dptr(query_start_loc, "query_start_loc"), _dptr(seq_lens, "seq_lens"),
+            _dptr(block_table, "block_table"), block_size, float(scale), _dptr(out, "out"), r, n, h, hkv, d, stride,
+            num_slots, qh, sh, int(max_query_len), int(max_seq_len), PA_DTYPE[q.dtype], _stream(stream), ref))
+        return out
     need = lib.paged_attention_workspace_bytes_ex(r, n, h, hkv, d, block_size, qh, sh, PA_DTYPE[q.dtype], ref)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
-    stride = block_table.shape[1] if block_table.dim() == 2 else 0
-    num_slots = k_cache.shape[0] * k_cache.shape[1]
     _check(lib.paged_attention_varlen_ex(
         _dptr(q, "q"), _dptr(k_cache, "k_cache"), _dptr(v_cache, "v_cache"),
         _dptr(query_start_loc, "query_start_loc"), _dptr(seq_lens, "seq_lens"), _dptr(block_table, "block_table"),

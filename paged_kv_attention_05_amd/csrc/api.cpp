@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -94,12 +95,8 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
               const int32_t* qsl, const int32_t* lens_host, int32_t dtype, int32_t window, int32_t graph_max,
               bool fp8, pa::Plan* out) {
   // with graph_max the launches are sized as if every seq_len were graph_max
-  std::vector<int32_t> capacity;
-  const int32_t* lens = lens_host;
-  if (graph_max > 0 && R > 0) {
-    capacity.assign((size_t)R, graph_max);
-    lens = capacity.data();
-  }
+  const bool sized_for_capacity = graph_max > 0;
+  auto len_of = [&](int32_t r) { return sized_for_capacity ? graph_max : lens_host[r]; };
   if (R < 0 || N < 0) return fail(PA_ERR_METADATA, "num_reqs and num_tokens must be >= 0");
   if (N > INT32_MAX) return fail(PA_ERR_SHAPE, "num_tokens must fit in int32");
   if (H <= 0 || Hkv <= 0 || H % Hkv != 0)
@@ -108,7 +105,8 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
     return fail(PA_ERR_SHAPE, "head_dim must be one of 8, 16, 32, 48, 64, 96, 128, 256");
   if (bs <= 0) return fail(PA_ERR_SHAPE, "block_size must be >= 1");
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "unknown dtype code");
-  if (R > 0 && (!qsl || !lens)) return fail(PA_ERR_NULL, "host copies of query_start_loc / seq_lens are required");
+  if (R > 0 && (!qsl || (!lens_host && !sized_for_capacity)))
+    return fail(PA_ERR_NULL, "host copies of query_start_loc / seq_lens are required");
   if (R == 0) {
     if (N != 0) return fail(PA_ERR_METADATA, "num_tokens > 0 with no requests");
   } else {
@@ -140,7 +138,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   int32_t span_max = 0;
   for (int32_t r = 0; r < R; ++r) {
     const int32_t t = qsl[r + 1] - qsl[r];
-    const int32_t L = lens[r];
+    const int32_t L = len_of(r);
     if (t < 0) return fail(PA_ERR_METADATA, "query_start_loc must be non-decreasing (request " + std::to_string(r) + ")");
     if (L < 0) return fail(PA_ERR_METADATA, "seq_lens must be >= 0 (request " + std::to_string(r) + ")");
     if (L > 0 && t > L)
@@ -168,11 +166,11 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   int32_t stage_w = 0;
   for (int32_t r = 0; r < R; ++r) {
     int32_t a, b, c, d;
-    pa::request_counts(p, qsl[r + 1] - qsl[r], lens[r], &a, &b, &c, &d);
+    pa::request_counts(p, qsl[r + 1] - qsl[r], len_of(r), &a, &b, &c, &d);
     ns += a; nm += b; np += c;
-    pa::small_groups(p, qsl[r + 1] - qsl[r], lens[r], &a, &b);
+    pa::small_groups(p, qsl[r + 1] - qsl[r], len_of(r), &a, &b);
     n1 += a; n3 += b;
-    const int32_t st = pa::staged_blocks(p, qsl[r + 1] - qsl[r], lens[r]);
+    const int32_t st = pa::staged_blocks(p, qsl[r + 1] - qsl[r], len_of(r));
     ng += st;
     stage_w = std::max(stage_w, st);
   }
@@ -206,6 +204,117 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.off_v16 = off;    off = align_up(off + 2 * (p.v16 ? (size_t)ng : 0) * bs * Hkv * D, 256);
   p.total_bytes = off;
   *out = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+// Scratch of paged_attention_varlen_noalloc: its workspace, for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy for the life of the process.
+// Host code never passes this name to a kernel (on the host it is only a stand-in for the
+// device symbol): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on its first use there.
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_LAUNCH, "device index out of range for the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_LAUNCH, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+// The attention call behind both entry points: validation, the plan, the launches.
+// scratch_call: the workspace is the library's own scratch array on the current device, of
+// workspace_bytes; its address is fetched once the batch is known to fit.
+int attention_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
+                   const int32_t* seq_lens, const int32_t* block_table, int32_t block_size, float scale, void* out,
+                   int32_t num_reqs, int64_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_table_stride, int64_t num_slots, const int32_t* query_start_loc_host,
+                   const int32_t* seq_lens_host, void* workspace, size_t workspace_bytes, int32_t dtype,
+                   hipStream_t stream, const pa_attention_options* options, bool scratch_call) {
+  if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
+  Options opt;
+  int rc = read_options(options, &opt, true);
+  if (rc != PA_OK) return rc;
+  const int32_t graph_max = opt.graph_max;
+  pa::Plan p;
+  rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                 query_start_loc_host, seq_lens_host, dtype, opt.window, opt.graph_max, opt.fp8, &p);
+  if (rc != PA_OK) return rc;
+  if (num_reqs == 0) return PA_OK;
+  if (!query_start_loc || !seq_lens || !block_table || (!workspace && !scratch_call))
+    return fail(PA_ERR_NULL, "null pointer argument");
+  if (num_tokens > 0 && (!q || !out || !k_cache || !v_cache)) return fail(PA_ERR_NULL, "null pointer argument");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "q, out, caches and workspace must be 16-byte aligned");
+  if (num_slots < block_size || num_slots % block_size != 0)
+    return fail(PA_ERR_SHAPE, "num_slots must be a positive multiple of block_size");
+  if (workspace_bytes < p.total_bytes)
+    return fail(PA_ERR_WORKSPACE, scratch_call ? "batch needs " + std::to_string(p.total_bytes) +
+                                                     " bytes of scratch, more than the no-alloc maximum of " +
+                                                     std::to_string(workspace_bytes) + " bytes"
+                                               : "workspace too small: need " + std::to_string(p.total_bytes) + " bytes");
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
+  if (scratch_call) {
+    rc = scratch_of_current_device(&workspace);
+    if (rc != PA_OK) return rc;
+  }
+  if (g_debug_checks && graph_max == 0) {   // (sized-for-capacity calls may be captured: no sync)
+    std::vector<int32_t> tb((size_t)num_reqs * block_table_stride);
+    if (!tb.empty() && hipMemcpy(tb.data(), block_table, sizeof(int32_t) * tb.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "debug check: copy of block_table failed");
+    const int64_t nb = num_slots / block_size;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      const int32_t used = (seq_lens_host[r] + block_size - 1) / block_size;
+      for (int32_t j = 0; j < used; ++j) {
+        const int32_t blk = tb[(size_t)r * block_table_stride + j];
+        if (blk < 0 || blk >= nb)
+          return fail(PA_ERR_RANGE, "block_table[" + std::to_string(r) + "][" + std::to_string(j) + "] out of range");
+      }
+    }
+  }
+  pa::AttnArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.qsl = query_start_loc; a.seq_lens = seq_lens; a.block_table = block_table; a.out = out;
+  a.bs = block_size; a.stride = block_table_stride; a.H = num_heads; a.Hkv = num_kv_heads;
+  a.g = p.g; a.D = head_dim; a.tile_tokens = p.tile_tokens; a.tile_heads = p.tile_heads;
+  a.split_keys = p.split_keys;
+  a.window = p.window;
+  a.totals = (const int32_t*)((const char*)workspace + p.off_req + sizeof(pa::ReqOffsets) * (size_t)num_reqs);
+  a.k_scale = opt.fp8 ? opt.k_scale : nullptr;
+  a.v_scale = opt.fp8 ? opt.v_scale : nullptr;
+  a.scale_log2e = scale * 1.4426950408889634f;
+
+  hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
+  if (e == hipSuccess && p.n_pf > 0)
+    e = timed(PA_KIND_PREFILL, stream, [&] {
+      return p.f8 ? pa::launch_stage_fp8(p, a, std::max(std::fabs(a.scale_log2e), 1e-30f), workspace, stream)
+                  : pa::launch_prefill_mfma(p, a, workspace, stream);
+    });
+  if (e == hipSuccess && p.n_small > 0)
+    e = timed(PA_KIND_SMALL, stream, [&] {
+      return p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)
+                                : pa::launch_small_valu(p, a, workspace, dtype, stream);
+    });
+  if (e == hipSuccess && p.n_merge > 0)
+    e = timed(PA_KIND_MERGE, stream, [&] { return pa::launch_merge(p, a, workspace, dtype, stream); });
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("attention launch: ") + hipGetErrorString(e));
   return PA_OK;
 }
 
@@ -389,66 +498,27 @@ int paged_attention_varlen_ex(const void* q, const void* k_cache, const void* v_
   g_last_error.clear();
   (void)max_query_len;
   (void)max_seq_len;
-  if (block_table_stride < 0) return fail(PA_ERR_METADATA, "block_table_stride must be >= 0");
-  Options opt;
-  int rc = read_options(options, &opt, true);
-  if (rc != PA_OK) return rc;
-  const int32_t graph_max = opt.graph_max;
-  pa::Plan p;
-  rc = make_plan(num_reqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                 query_start_loc_host, seq_lens_host, dtype, opt.window, opt.graph_max, opt.fp8, &p);
-  if (rc != PA_OK) return rc;
-  if (num_reqs == 0) return PA_OK;
-  if (!query_start_loc || !seq_lens || !block_table || !workspace) return fail(PA_ERR_NULL, "null pointer argument");
-  if (num_tokens > 0 && (!q || !out || !k_cache || !v_cache)) return fail(PA_ERR_NULL, "null pointer argument");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
-    return fail(PA_ERR_SHAPE, "q, out, caches and workspace must be 16-byte aligned");
-  if (num_slots < block_size || num_slots % block_size != 0)
-    return fail(PA_ERR_SHAPE, "num_slots must be a positive multiple of block_size");
-  if (workspace_bytes < p.total_bytes)
-    return fail(PA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.total_bytes) + " bytes");
-  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
-  if (g_debug_checks && graph_max == 0) {   // (sized-for-capacity calls may be captured: no sync)
-    std::vector<int32_t> tb((size_t)num_reqs * block_table_stride);
-    if (!tb.empty() && hipMemcpy(tb.data(), block_table, sizeof(int32_t) * tb.size(), hipMemcpyDeviceToHost) != hipSuccess)
-      return fail(PA_ERR_LAUNCH, "debug check: copy of block_table failed");
-    const int64_t nb = num_slots / block_size;
-    for (int32_t r = 0; r < num_reqs; ++r) {
-      const int32_t used = (seq_lens_host[r] + block_size - 1) / block_size;
-      for (int32_t j = 0; j < used; ++j) {
-        const int32_t blk = tb[(size_t)r * block_table_stride + j];
-        if (blk < 0 || blk >= nb)
-          return fail(PA_ERR_RANGE, "block_table[" + std::to_string(r) + "][" + std::to_string(j) + "] out of range");
-      }
-    }
-  }
-  pa::AttnArgs a{};
-  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
-  a.qsl = query_start_loc; a.seq_lens = seq_lens; a.block_table = block_table; a.out = out;
-  a.bs = block_size; a.stride = block_table_stride; a.H = num_heads; a.Hkv = num_kv_heads;
-  a.g = p.g; a.D = head_dim; a.tile_tokens = p.tile_tokens; a.tile_heads = p.tile_heads;
-  a.split_keys = p.split_keys;
-  a.window = p.window;
-  a.totals = (const int32_t*)((const char*)workspace + p.off_req + sizeof(pa::ReqOffsets) * (size_t)num_reqs);
-  a.k_scale = opt.fp8 ? opt.k_scale : nullptr;
-  a.v_scale = opt.fp8 ? opt.v_scale : nullptr;
-  a.scale_log2e = scale * 1.4426950408889634f;
+  return attention_impl(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, block_size, scale, out, num_reqs,
+                        num_tokens, num_heads, num_kv_heads, head_dim, block_table_stride, num_slots,
+                        query_start_loc_host, seq_lens_host, workspace, workspace_bytes, dtype, stream, options, false);
+}
 
-  hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
-  if (e == hipSuccess && p.n_pf > 0)
-    e = timed(PA_KIND_PREFILL, stream, [&] {
-      return p.f8 ? pa::launch_stage_fp8(p, a, std::max(std::fabs(a.scale_log2e), 1e-30f), workspace, stream)
-                  : pa::launch_prefill_mfma(p, a, workspace, stream);
-    });
-  if (e == hipSuccess && p.n_small > 0)
-    e = timed(PA_KIND_SMALL, stream, [&] {
-      return p.decode_kind == 1 ? pa::launch_small_mfma(p, a, workspace, stream)
-                                : pa::launch_small_valu(p, a, workspace, dtype, stream);
-    });
-  if (e == hipSuccess && p.n_merge > 0)
-    e = timed(PA_KIND_MERGE, stream, [&] { return pa::launch_merge(p, a, workspace, dtype, stream); });
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("attention launch: ") + hipGetErrorString(e));
-  return PA_OK;
+int paged_attention_varlen_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int32_t* block_table, int32_t block_size, float scale, void* out,
+                                   int32_t num_reqs, int64_t num_tokens, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_table_stride,
+                                   int64_t num_slots, const int32_t* query_start_loc_host,
+                                   const int32_t* seq_lens_host, int32_t max_query_len,
+                                   int32_t max_seq_len, int32_t dtype, hipStream_t stream,
+                                   const pa_attention_options* options) {
+  g_last_error.clear();
+  (void)max_query_len;
+  (void)max_seq_len;
+  return attention_impl(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, block_size, scale, out, num_reqs,
+                        num_tokens, num_heads, num_kv_heads, head_dim, block_table_stride, num_slots,
+                        query_start_loc_host, seq_lens_host, nullptr, (size_t)PA_NOALLOC_SCRATCH_BYTES, dtype,
+                        stream, options, true);
 }
 
 int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream) {

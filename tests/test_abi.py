@@ -180,3 +180,30 @@ def test_no_kernel_spills_registers():
     for k in kernels:
         assert int(k["scratch"]) == 0 and int(k["vgpr_spill"]) == 0, k["name"]
         assert int(k["lds"]) <= 160 * 1024, k["name"]
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch():
+    """The no-alloc entry point sizes the batch from the host metadata before it looks up its
+    scratch array: 2000 decodes of 32768 tokens need far more than PA_NOALLOC_SCRATCH_BYTES of
+    split partials and are refused with PA_ERR_WORKSPACE (no device is touched)."""
+    lib = pk.load_library()
+    R, L = 2000, 32768
+    qsl = list(range(R + 1))
+    lens = [L] * R
+    need = lib.paged_attention_workspace_bytes(R, R, 64, 8, 128, 16, _host(qsl), _host(lens), 1)
+    assert need > pk.NOALLOC_SCRATCH_BYTES
+    rc = lib.paged_attention_varlen_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1, FAKE, R, R, 64, 8, 128,
+                                            L // 16, (L // 16 + 1) * 16, _host(qsl), _host(lens), 1, L, 1, None,
+                                            None)
+    assert rc == -5
+    msg = lib.paged_attn_last_error().decode()
+    assert "no-alloc maximum" in msg and str(pk.NOALLOC_SCRATCH_BYTES) in msg
+    # malformed metadata is refused the same way as by the workspace entry points
+    assert lib.paged_attention_varlen_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1, FAKE, 1, 6, 8, 2, 128, 4,
+                                              1024, _host([0, 6]), _host([5]), 0, 0, 1, None, None) == -4
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "paged_attn.h")).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pk.NOALLOC_SCRATCH_BYTES
