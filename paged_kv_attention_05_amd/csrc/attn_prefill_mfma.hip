@@ -13,7 +13,9 @@
 //
 // Data movement: each 64-key K and V tile goes from HBM straight into LDS with the gfx950
 // direct loads (global_load_lds_dwordx4, 16 bytes per lane, no register staging), into rings
-// of three tiles, so later tiles stream in while the current one is computed.  K comes from
+// of three tiles, so later tiles stream in while the current one is computed.  A load's
+// block address (base + block id x block bytes) is formed on the scalar unit from the
+// wave's own two block-table entries per tile.  K comes from
 // the pool through the block table; V from an fp16 copy of the request's blocks made just
 // before (v16_stage.hip).  An LDS row is
 // one key's 256 bytes; its sixteen 16-byte chunks are stored XOR-swizzled (chunk c of row r
@@ -113,6 +115,21 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, unsi
   // (readfirstlane returns int: go through uint32_t so the low word is not sign-extended)
   const uint64_t sbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
                          (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr(lds_wave_base)), "v"(voff),
+               "s"(sbase)
+               : "memory");
+}
+
+// The same load from base + idx * stride (bytes; base as two 32-bit halves, idx and stride
+// wave-uniform): the block address is formed by the scalar unit, with no vector round trip.
+__device__ __forceinline__ void load_lds16_at(uint32_t base_lo, uint32_t base_hi, uint32_t idx, uint32_t stride,
+                                              uint32_t voff, unsigned char* lds_wave_base) {
+  uint32_t lo, hi;
+  asm volatile("s_mul_i32 %0, %2, %3\n\ts_mul_hi_u32 %1, %2, %3\n\ts_add_u32 %0, %0, %4\n\ts_addc_u32 %1, %1, %5"
+               : "=&s"(lo), "=&s"(hi)
+               : "s"(idx), "s"(stride), "s"(base_lo), "s"(base_hi)
+               : "scc");
+  const uint64_t sbase = ((uint64_t)hi << 32) | lo;
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr(lds_wave_base)), "v"(voff),
                "s"(sbase)
                : "memory");
@@ -230,16 +247,26 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     // with a scalar load, which does not wait behind the tile loads in flight
     const __attribute__((address_space(4))) int32_t* e =
         (const __attribute__((address_space(4))) int32_t*)(table_row + 4 * j);
+    if constexpr (F16) return Blocks{e[w >> 2], e[(w >> 2) + 2], 0, 0};   // this wave's two blocks
     return Blocks{e[0], e[1], e[2], e[3]};
   };
   // block of instruction u within the tile: wave-uniform ((w + WAVES*u) / 4)
   auto pick = [&](const Blocks& bl, int u) -> int32_t {
+    if constexpr (F16) return u == 0 ? bl.b0 : bl.b1;
     const int bi = WAVES == 4 ? u : ((w >> 2) + (WAVES / 4) * u);
     return bi == 0 ? bl.b0 : bi == 1 ? bl.b1 : bi == 2 ? bl.b2 : bl.b3;
   };
+  const uint32_t blk_bytes = (uint32_t)(blk_stride * 2);
+  const uint64_t kc_b = (uint64_t)(uintptr_t)kc;
+  const uint32_t kc_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)kc_b);
+  const uint32_t kc_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(kc_b >> 32));
   auto issue = [&](const __bf16* base, int32_t j, const Blocks& bl, unsigned char* dst) {
     j += t0;
-    if (j * kBK + kBK <= kend) {
+    if (F16 && j * kBK + kBK <= kend) {
+#pragma unroll
+      for (int u = 0; u < UK; ++u)
+        load_lds16_at(kc_lo, kc_hi, (uint32_t)pick(bl, u), blk_bytes, lane_off_b, dst + (w + WAVES * u) * 1024);
+    } else if (j * kBK + kBK <= kend) {
 #pragma unroll
       for (int u = 0; u < UK; ++u)
         load_lds16(base + (int64_t)pick(bl, u) * blk_stride, lane_off_b, dst + (w + WAVES * u) * 1024);
@@ -265,15 +292,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   static_assert(WAVES % 4 == 0, "a wave's V pieces share one dim range");
   const int32_t stage0 = F16 ? __builtin_amdgcn_readfirstlane(a.req[r_id].stage) - v16_first_block(a.window, t, L) : 0;
   const uint16_t* v16 = F16 ? (const uint16_t*)a.v_staged + (int64_t)stage0 * blk_stride + (int64_t)hkv * D * kBlk : nullptr;
+  const uint64_t v16_b = (uint64_t)(uintptr_t)v16;
+  const uint32_t v16_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v16_b);
+  const uint32_t v16_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v16_b >> 32));
   const int vdim = 32 * (w & 3) + (lane >> 1);
   const uint32_t v16_lane_off_b = (uint32_t)(vdim * 32 + 16 * ((lane & 1) ^ ((vdim >> 3) & 1)));
   auto issue_v = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
     if constexpr (F16) {
-      const uint16_t* tile = v16 + (int64_t)(4 * (j + t0)) * blk_stride;
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
         const int bi = (w + WAVES * u) >> 2;
-        load_lds16(tile + (int64_t)bi * blk_stride, v16_lane_off_b, dst + (w + WAVES * u) * 1024);
+        load_lds16_at(v16_lo, v16_hi, (uint32_t)(4 * (j + t0) + bi), blk_bytes, v16_lane_off_b,
+                      dst + (w + WAVES * u) * 1024);
       }
     } else {
       issue(vc, j, bl, dst);
@@ -304,8 +334,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   float lsum2 = 0.f;                                          // a second row-sum accumulator
   const int G = lane >> 4, i16 = lane & 15;
 
-  // S^T of one K tile (keys 64j .. 64j+63, two halves of 32 keys)
-  // (the two halves alternate, so consecutive matrix instructions are independent)
   // Per-lane LDS read addresses at ring slot 0, passed through an empty asm so the compiler
   // keeps them as they are and adds the slot and chunk offsets as read-instruction immediates
   // (no extra address registers per ring slot).
@@ -337,32 +365,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // the ring slot, the K/V half and the key run are immediates
   uint32_t scoff = lds_addr(smem + SC_RING) + 16 * h;
   asm volatile("" : "+v"(scoff));
-  auto qk = [&](int b, f32x16* s, auto&& after_group) {
-    // K reads in groups of two k-chunks (four reads), each group issued one group ahead of
-    // its products; scheduling fences keep that order
-    auto read_k = [&](int g, bf16x8* ka) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = 2 * g + (e >> 1), sh = e & 1;
-        ka[e] = lds_read16(koff[kk] + b * C::TILE + 32 * sh * C::ROW);
-      }
-    };
-    bf16x8 ka[2][4];
-    read_k(0, ka[0]);
-#pragma unroll
-    for (int g = 0; g < C::KC / 2; ++g) {
-      if (g + 1 < C::KC / 2) read_k(g + 1, ka[(g + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = 2 * g + (e >> 1), sh = e & 1;
-        s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], f32x16{}, 0, 0, 0)
-                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][e], qf[kk], s[sh], 0, 0, 0);
-      }
-      after_group(g);                                  // vector work issued under the products
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
 
 
@@ -401,7 +403,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   }
   Blocks blV = fetch_blocks(1);                              // blocks of V(i+1)
   Blocks blK = fetch_blocks(2);                              // blocks of K(i+2)
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // the V slot that the first matrix phase multiplies by P = 0 holds zeros (finite)
+  for (int c = tid; c < C::TILE / 16; c += NT) *(u32x4*)(vbuf(NBUF - 1) + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // P = i % 3 is a compile-time constant in every call below (the slot loop is unrolled by
   // three), so all LDS addresses are per-lane offsets plus immediates
   auto issue_slot = [&](int32_t i, auto par) {
@@ -419,6 +423,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // P of the last vector phase: fp16 pairs (fast kernel), or the bf16 high parts with pl
   // holding the bf16 roundings of the remainders
   u32x4 pb[4], pl[F16 ? 1 : 4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pb[c] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < (F16 ? 1 : 4); ++c) pl[c] = u32x4{0u, 0u, 0u, 0u};
   // V^T operand of one 16-key chunk for the four d tiles (eight transpose reads)
   auto read_v = [&](int b, int qc, u32x4* va) {
 #pragma unroll
@@ -433,42 +441,67 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       }
     }
   };
+  // The matrix phase as one stream of eight operand groups: the four V^T chunks of
+  // O += V(i-1) P(i-1), then the four K groups of S(i) = QK^T (two k-chunks of both 32-key
+  // halves, so consecutive products accumulate into different tiles).  Each group's LDS
+  // reads are issued one group before its products, across the PV/QK boundary too, and
+  // scheduling fences keep that order: the matrix core does not wait on LDS.
+  // One code path for every tile: at i = 0 the PV products run on a zeroed V slot with
+  // P = 0, and at i = ntiles the scores of a stale K slot are never used.
   auto phase_m = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
-    // PV first: P(i-1) is dead before S(i) is produced, so the two share registers
-    if (i >= 1) {
-      // O^T += V^T P^T over the four 16-key chunks, per chunk one product per d tile (two in
-      // the bf16 kernel: high parts, then low parts), so consecutive matrix instructions
-      // accumulate into different tiles.  The next chunk's V^T reads are issued before this
-      // chunk's products (scheduling fences keep that order): the matrix core does not wait
-      // on LDS.
-      constexpr int Vb = (P + NBUF - 1) % NBUF;
-      u32x4 va[2][C::DT];
-      read_v(Vb, 0, va[0]);
-      __builtin_amdgcn_sched_barrier(0);
+    constexpr int Vb = (P + NBUF - 1) % NBUF;
+    u32x4 buf[2][4];
+    auto rd = [&](int q, u32x4* bb) {
+      if (q < 4) {
+        read_v(Vb, q, bb);
+      } else {
 #pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        if (qc < 3) read_v(Vb, qc + 1, va[(qc + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 4; ++e) {
+          const int kk = 2 * (q - 4) + (e >> 1), sh = e & 1;
+          bb[e] = __builtin_bit_cast(u32x4, lds_read16(koff[kk] + P * C::TILE + 32 * sh * C::ROW));
+        }
+      }
+    };
+    rd(0, buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q + 1 < 8) rd(q + 1, buf[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4* bb = buf[q & 1];
+      if (q < 4) {
+        // O^T += V^T P^T for 16-key chunk q, one product per d tile (two in the bf16 kernel:
+        // high parts, then low parts)
         if constexpr (F16) {
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[qc & 1][dt]),
-                                                           __builtin_bit_cast(f16x8, pb[qc]), o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, bb[dt]),
+                                                           __builtin_bit_cast(f16x8, pb[q]), o[dt], 0, 0, 0);
         } else {
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[qc & 1][dt]),
-                                                            __builtin_bit_cast(bf16x8, pb[qc]), o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bb[dt]),
+                                                            __builtin_bit_cast(bf16x8, pb[q]), o[dt], 0, 0, 0);
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[qc & 1][dt]),
-                                                            __builtin_bit_cast(bf16x8, pl[qc]), o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bb[dt]),
+                                                            __builtin_bit_cast(bf16x8, pl[q]), o[dt], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // S^T of K tile i, k-chunks 2g and 2g+1 of both 32-key halves
+        const int g = q - 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = 2 * g + (e >> 1), sh = e & 1;
+          s[sh] = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bb[e]), qf[kk],
+                                                                    f32x16{}, 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bb[e]), qf[kk],
+                                                                    s[sh], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (i < ntiles) qk(P, s, [](int) {});
   };
   auto phase_x = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
