@@ -32,8 +32,13 @@ PEAK_F32_TFLOPS = 157.3         # fp32 vector
 PREFILL_MIN_COLS = 64           # the library sends requests with more query rows x group heads
                                 # than this to the prefill kernel (bf16, head_dim 128)
 METRIC = "paged-attn decode KV GB/s + prefill TFLOP/s, % of MI355X peak"
-KERNEL_SOURCES = {"prefill": "attn_prefill_mfma.hip", "small": "attn_decode_mfma.hip",
-                  "kv_write": "kv_write.hip", "merge": "attn_valu.hip", "plan": "plan.hip"}
+# the sources of each kernel kind (its staging kernels included), plus the ones every kind
+# depends on (shared formulas, launch configuration): a committed counter figure is used only
+# while all of them are unchanged
+KERNEL_SOURCES = {"prefill": ["attn_prefill_mfma.hip", "v16_stage.hip", "fp8_stage.hip"],
+                  "small": ["attn_decode_mfma.hip"], "kv_write": ["kv_write.hip"], "merge": ["attn_valu.hip"],
+                  "plan": ["plan.hip"]}
+COMMON_SOURCES = ["pa_internal.h", "api.cpp"]
 
 
 def eprint(*a):
@@ -41,15 +46,17 @@ def eprint(*a):
 
 
 def kernel_sha(kind: str) -> str:
-    path = os.path.join(ROOT, "paged_kv_attention_05_amd", "csrc", KERNEL_SOURCES[kind])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind] + COMMON_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_05_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def measured(file: str, field: str, kind: str, workload: str):
+    """A per-launch figure from a committed rocprofv3 counter summary (profiles/<file>), if it
+    was taken on the current sources of that kernel kind; else None."""
+    path = os.path.join(ROOT, "profiles", file)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -57,7 +64,18 @@ def measured_traffic(kind: str, workload: str):
     entry = data.get(workload, {}).get(kind)
     if not entry or entry.get("kernel_sha") != kernel_sha(kind):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get(field)
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading)."""
+    return measured("traffic.json", "hbm_bytes_per_launch", kind, workload)
+
+
+def measured_mfma_busy(kind: str, workload: str):
+    """Fraction of cycles the matrix cores are busy during the kind's launches
+    (SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs / (GRBM_GUI_ACTIVE per XCD x SIMDs))."""
+    return measured("mfma.json", "mfma_busy", kind, workload)
 
 
 def main() -> int:
@@ -287,8 +305,10 @@ def main() -> int:
         roof = {"kernel": "kv_quant_fp8" if fp8 else "kv_copy16", "bound": "hbm", "achieved": gb, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gb / PEAK_HBM_GBPS, "algorithmic_per_launch": w_write["bytes"],
                 "avg_launch_ms": kern_avg["kv_write"]}
-    roof["traffic"] = measured_traffic(dom, args.workload + (f"_window{args.window}" if args.window else "")
-                                       + ("_fp8" if fp8 else ""))
+    wl_key = args.workload + (f"_window{args.window}" if args.window else "") + ("_fp8" if fp8 else "")
+    roof["traffic"] = measured_traffic(dom, wl_key)
+    # matrix-core busy fraction of a matrix-core-bound kernel, from its committed counters
+    roof["mfma_busy"] = measured_mfma_busy(dom, wl_key) if roof["bound"] == "mfma" else None
 
     # mixed batches: the decode-row and the prefill-row requests as sub-calls of their own
     # (attention only, over the pool the steps wrote)
@@ -457,24 +477,29 @@ def hbm_probe(torch, pk, dev, gib=4):
 def mfma_probe(torch, pk, dev, iters=4096):
     """Matrix-core rate the chip sustains beside the 2.5 PFLOP/s specification: the library's
     probe of back-to-back bf16 32x32x16 products with no memory traffic (best over two grid
-    sizes, best of 5 each)."""
+    sizes, best of 5 each), on small-integer operands and on random ones like attention's
+    (the chip clocks down under the latter)."""
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    rates = {}
-    for grid in (1024, 2048):
-        flops = pk.mfma_probe(iters, grid, sink)
-        times = []
-        for _ in range(5):
-            a.record()
-            pk.mfma_probe(iters, grid, sink)
-            b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        rates[grid] = flops / (min(times) * 1e-3) / 1e12
-    top = max(rates, key=rates.get)
-    return {"tflops": rates[top], "grid": top, "tflops_by_grid": {str(k): v for k, v in rates.items()},
-            "how": f"paged_mfma_probe: 512-thread workgroups, {iters} rounds of 8 independent "
-                   "32x32x16 bf16 products per wave, no memory traffic; best of 5"}
+    out = {}
+    for label, rnd in (("integer_operands", False), ("random_operands", True)):
+        rates = {}
+        for grid in (1024, 2048):
+            flops = pk.mfma_probe(iters, grid, sink, random_operands=rnd)
+            times = []
+            for _ in range(5):
+                a.record()
+                pk.mfma_probe(iters, grid, sink, random_operands=rnd)
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            rates[grid] = flops / (min(times) * 1e-3) / 1e12
+        top = max(rates, key=rates.get)
+        out[label] = {"tflops": rates[top], "grid": top, "tflops_by_grid": {str(k): v for k, v in rates.items()}}
+    out["tflops"] = out["integer_operands"]["tflops"]
+    out["how"] = (f"paged_mfma_probe: 512-thread workgroups, {iters} rounds of 8 independent 32x32x16 bf16 "
+                  "products per wave, no memory traffic, operands small integers or random bf16; best of 5")
+    return out
 
 
 def _cpu_model():

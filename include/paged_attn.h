@@ -310,11 +310,13 @@ int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t
  * its clock and power limits, beside the 2.5 PFLOP/s specification the prefill kernel is
  * measured against.
  *   iters  1 .. 2^20;  grid 1 .. 65536.
+ *   data   0: operands are small integers (0 .. 7); 1: random bf16 values in [-2, 2), as
+ *          attention's are (the sustained rate depends on the operands' bits).
  *   sink   one device uint32 the kernel may write (to keep its products alive).
  *   flops  optional host int64: receives the launch's floating-point operation count.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_LAUNCH.
  */
-int paged_mfma_probe(int32_t iters, int32_t grid, uint32_t* sink, int64_t* flops, hipStream_t stream);
+int paged_mfma_probe(int32_t iters, int32_t grid, int32_t data, uint32_t* sink, int64_t* flops, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -65,7 +65,7 @@ def load_library(path: str = LIB_PATH):
     lib.paged_hbm_read_probe.restype = ctypes.c_int
     lib.paged_hbm_read_probe.argtypes = [P, I64, P, I32, P]
     lib.paged_mfma_probe.restype = ctypes.c_int
-    lib.paged_mfma_probe.argtypes = [I32, I32, P, P, P]
+    lib.paged_mfma_probe.argtypes = [I32, I32, I32, P, P, P]
     lib.paged_copy_blocks.restype = ctypes.c_int
     lib.paged_copy_blocks.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
     lib.paged_attention_workspace_bytes.restype = SZ
@@ -138,12 +138,13 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None
                                     int(grid), _stream(stream)))
 
 
-def mfma_probe(iters: int, grid: int, sink: torch.Tensor, stream=None) -> int:
-    """Run back-to-back bf16 matrix products (measurement of the sustained matrix-core rate);
-    returns the launch's floating-point operation count."""
+def mfma_probe(iters: int, grid: int, sink: torch.Tensor, stream=None, random_operands: bool = False) -> int:
+    """Run back-to-back bf16 matrix products (measurement of the sustained matrix-core rate),
+    on small-integer or random operands; returns the launch's floating-point operation count."""
     lib = load_library()
     flops = ctypes.c_int64(0)
-    _check(lib.paged_mfma_probe(int(iters), int(grid), _dptr(sink, "sink"), ctypes.byref(flops), _stream(stream)))
+    _check(lib.paged_mfma_probe(int(iters), int(grid), 1 if random_operands else 0, _dptr(sink, "sink"),
+                                ctypes.byref(flops), _stream(stream)))
     return flops.value
 
 

@@ -531,13 +531,14 @@ int paged_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t
   return PA_OK;
 }
 
-int paged_mfma_probe(int32_t iters, int32_t grid, uint32_t* sink, int64_t* flops, hipStream_t stream) {
+int paged_mfma_probe(int32_t iters, int32_t grid, int32_t data, uint32_t* sink, int64_t* flops, hipStream_t stream) {
   g_last_error.clear();
   if (!sink) return fail(PA_ERR_NULL, "null pointer argument");
   if (iters < 1 || iters > (1 << 20)) return fail(PA_ERR_SHAPE, "iters must be in 1 .. 2^20");
   if (grid < 1 || grid > 65536) return fail(PA_ERR_SHAPE, "grid must be in 1 .. 65536");
+  if (data != 0 && data != 1) return fail(PA_ERR_SHAPE, "data must be 0 (small integers) or 1 (random values)");
   if (flops) *flops = pa::mfma_probe_flops(iters, grid);
-  const hipError_t e = pa::launch_mfma_probe(iters, sink, grid, stream);
+  const hipError_t e = pa::launch_mfma_probe(iters, data, sink, grid, stream);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, std::string("matrix probe launch: ") + hipGetErrorString(e));
   return PA_OK;
 }

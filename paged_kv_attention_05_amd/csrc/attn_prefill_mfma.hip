@@ -124,10 +124,12 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, unsi
 // wave-uniform): the block address is formed by the scalar unit, with no vector round trip.
 __device__ __forceinline__ void load_lds16_at(uint32_t base_lo, uint32_t base_hi, uint32_t idx, uint32_t stride,
                                               uint32_t voff, unsigned char* lds_wave_base) {
+  // (readfirstlane: the operands are wave-uniform; it makes sure they sit in scalar registers)
   uint32_t lo, hi;
   asm volatile("s_mul_i32 %0, %2, %3\n\ts_mul_hi_u32 %1, %2, %3\n\ts_add_u32 %0, %0, %4\n\ts_addc_u32 %1, %1, %5"
                : "=&s"(lo), "=&s"(hi)
-               : "s"(idx), "s"(stride), "s"(base_lo), "s"(base_hi)
+               : "s"(__builtin_amdgcn_readfirstlane(idx)), "s"(__builtin_amdgcn_readfirstlane(stride)),
+                 "s"(__builtin_amdgcn_readfirstlane(base_lo)), "s"(__builtin_amdgcn_readfirstlane(base_hi))
                : "scc");
   const uint64_t sbase = ((uint64_t)hi << 32) | lo;
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr(lds_wave_base)), "v"(voff),

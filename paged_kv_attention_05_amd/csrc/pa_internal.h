@@ -246,7 +246,7 @@ hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStre
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtype, hipStream_t s);
 hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t s);
-hipError_t launch_mfma_probe(int32_t iters, uint32_t* sink, int32_t grid, hipStream_t s);
+hipError_t launch_mfma_probe(int32_t iters, int32_t data, uint32_t* sink, int32_t grid, hipStream_t s);
 int64_t mfma_probe_flops(int32_t iters, int32_t grid);
 // fp8 pools: stage the prefill requests' blocks as bf16 codes and scaled scales, then run the
 // prefill kernel on the staged copy

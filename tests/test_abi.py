@@ -156,11 +156,12 @@ def test_read_probe_rejects_bad_arguments():
 def test_mfma_probe_rejects_bad_arguments():
     lib = pk.load_library()
     sink = ctypes.c_void_p(0x2000)                 # never dereferenced: validation fails first
-    assert lib.paged_mfma_probe(16, 64, None, None, None) == -1
-    assert lib.paged_mfma_probe(0, 64, sink, None, None) == -2
-    assert lib.paged_mfma_probe(1 << 21, 64, sink, None, None) == -2
-    assert lib.paged_mfma_probe(16, 0, sink, None, None) == -2
-    assert lib.paged_mfma_probe(16, 70000, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 64, 0, None, None, None) == -1
+    assert lib.paged_mfma_probe(0, 64, 0, sink, None, None) == -2
+    assert lib.paged_mfma_probe(1 << 21, 64, 0, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 0, 0, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 70000, 0, sink, None, None) == -2
+    assert lib.paged_mfma_probe(16, 64, 2, sink, None, None) == -2
 
 
 def test_no_kernel_spills_registers():

@@ -778,7 +778,8 @@ def test_mfma_probe_runs():
     import paged_kv_attention_05_amd as pk
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for iters, grid in ((1, 1), (64, 256), (16, 2048)):
-        assert pk.mfma_probe(iters, grid, sink) == grid * 8 * iters * 8 * 2 * 32 * 32 * 16
+        for rnd in (False, True):
+            assert pk.mfma_probe(iters, grid, sink, random_operands=rnd) == grid * 8 * iters * 8 * 2 * 32 * 32 * 16
     torch.cuda.synchronize()
 
 
