@@ -146,8 +146,9 @@ size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int
  * (query heads grouped contiguously onto KV heads).  Requests with seq_len 0 or no rows
  * (padding) produce zero rows.  Arithmetic is float32: bfloat16 inputs feed the matrix
  * cores with float32 accumulation.  In the PV product, probabilities carry at least 11
- * significant bits: fp16 probabilities against V converted exactly to fp16 (prefill chunks,
- * while |v| <= 65504), else a bf16 pair (high part and the bf16 rounding of the remainder).
+ * significant bits: fp16 probabilities against V converted to fp16 (prefill chunks, while
+ * |v| <= 65504; the conversion is exact for |v| >= 2^-14 and moves smaller values by at most
+ * 2^-25), else a bf16 pair (high part and the bf16 rounding of the remainder).
  * out is rounded to nearest-even.
  *
  * Supported: head_dim in {8, 16, 32, 48, 64, 96, 128, 256}; block_size >= 1 (the bf16
