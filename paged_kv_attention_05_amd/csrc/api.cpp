@@ -128,7 +128,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
                     ? pa::prefill_tile_tokens(p.g) : 0;
   p.f8 = fp8 ? 1 : 0;
-  p.v16 = (!fp8 && p.pf_tokens > 0) ? 1 : 0;
+  p.v16 = p.pf_tokens > 0 ? 1 : 0;
   p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs)) ? 1 : 0;
   if (fp8 && p.decode_kind != 1)
     return fail(PA_ERR_DTYPE, "fp8 pools need dtype bf16, block_size 16, head_dim 64 or 128 and the automatic path");
@@ -163,22 +163,19 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   p.split_keys = split;
 
   int64_t ns = 0, nm = 0, np = 0, ng = 0, n1 = 0, n3 = 0;
-  int32_t stage_w = 0;
   for (int32_t r = 0; r < R; ++r) {
     int32_t a, b, c, d;
     pa::request_counts(p, qsl[r + 1] - qsl[r], len_of(r), &a, &b, &c, &d);
     ns += a; nm += b; np += c;
     pa::small_groups(p, qsl[r + 1] - qsl[r], len_of(r), &a, &b);
     n1 += a; n3 += b;
-    const int32_t st = pa::staged_blocks(p, qsl[r + 1] - qsl[r], len_of(r));
-    ng += st;
-    stage_w = std::max(stage_w, st);
+    ng += pa::staged_blocks(p, qsl[r + 1] - qsl[r], len_of(r));
   }
   if (ns > INT32_MAX / 2 || nm > INT32_MAX / 2 || np > INT32_MAX / 2 || ng > INT32_MAX / 2)
     return fail(PA_ERR_SHAPE, "batch too large for the work lists");
   // the prefill kernel addresses staged scales with 32-bit offsets per workgroup
   if (p.f8 && ng * 2 * Hkv * 16 * 4 > (int64_t)INT32_MAX) return fail(PA_ERR_SHAPE, "fp8 prefill: too many staged blocks");
-  p.n_small = ns; p.n_merge = nm; p.n_pf = np; p.n_stage = ng; p.stage_w = stage_w;
+  p.n_small = ns; p.n_merge = nm; p.n_pf = np; p.n_stage = ng;
   p.n_g1 = n1; p.n_g3 = n3;
 
   size_t off = 0;
@@ -194,13 +191,13 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   const bool mfma_lists = p.decode_kind == 1;
   p.off_g1 = off;    off = align_up(off + sizeof(pa::SmallItem) * (size_t)(mfma_lists ? n1 : 0), 256);
   p.off_g3 = off;    off = align_up(off + sizeof(pa::SmallItem) * (size_t)(mfma_lists ? n3 : 0), 256);
-  // fp8 pools: staged bf16 codes, scales and block table of the prefill requests
+  // fp8 pools: staged bf16 codes (K, and V for the bf16 redo kernel) and scales of the
+  // prefill requests
   const size_t ng8 = p.f8 ? (size_t)ng : 0;
-  p.off_f8_tab = off; off = align_up(off + 4 * (size_t)(ng8 > 0 ? R : 0) * stage_w, 256);
   p.off_f8_k = off;   off = align_up(off + 2 * ng8 * bs * Hkv * D, 256);
   p.off_f8_v = off;   off = align_up(off + 2 * ng8 * bs * Hkv * D, 256);
   p.off_f8_s = off;   off = align_up(off + 4 * ng8 * 2 * Hkv * bs, 256);
-  // bf16 pools: the fp16 copy of the prefill requests' V blocks
+  // the fp16 copy of the prefill requests' V blocks (fp8 pools: codes times scales)
   p.off_v16 = off;    off = align_up(off + 2 * (p.v16 ? (size_t)ng : 0) * bs * Hkv * D, 256);
   p.total_bytes = off;
   *out = p;

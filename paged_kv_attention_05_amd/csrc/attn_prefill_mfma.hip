@@ -143,23 +143,24 @@ __device__ __forceinline__ void load_lds4(const void* g, unsigned char* lds_wave
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds_wave_base)), "v"(g) : "memory");
 }
 
-// F16 = true: the fast kernel.  V comes already in fp16, from the copy that stage_v16
-// (v16_stage.hip) made of the request's blocks: request r's block j is staged block
-// req[r].stage + j, so V needs no table lookup.  P goes to the matrix cores as fp16.  An
-// item whose V leaves fp16's range (|v| > 65504) was flagged by the staging kernel
-// (wide[lin] = 1); its output is rewritten by the F16 = false kernel, launched right after
-// on the same stream, which reads V in bf16 from the pool and carries P as a bf16 pair.
+// F16 = true: the fast kernels.  V comes already in fp16, from the copy that the staging
+// kernel made of the request's blocks (v16_stage.hip for bf16 pools, fp8_stage.hip for fp8
+// pools): request r's block j is staged block req[r].stage + j - first, so V needs no table
+// lookup.  P goes to the matrix cores as fp16.  An item whose V leaves fp16's range
+// (|v| > 65504) was flagged by the staging kernel (wide[lin] = 1); its output is rewritten
+// by the F16 = false kernel of the same pool kind, launched right after on the same stream,
+// which reads V in bf16 and carries P as a bf16 pair; its other workgroups exit at once.
 //
-// F8 = true (with F16 = false): fp8 pools.  The kernel reads the staged bf16 copy of the
-// request's codes (exact) through the staged block table, and the staged per-key scales:
-// each score is multiplied by its key's K scale (which carries |scale| log2 e) and each
-// probability by its key's V scale before the PV product (the row sum takes the
-// probabilities alone), as the gathered rows of "ReferenceBackend.dequantize" are the codes
-// times their scales.  Scales of a tile come into LDS with its V loads (waves 0 and 1).
+// F8 = true: fp8 pools.  K comes from the staged bf16 copy of the codes (exact), at staged
+// block numbers (no table), and each score is multiplied by its key's staged K scale (which
+// carries |scale| log2 e), as the gathered rows of "ReferenceBackend.dequantize" are the
+// codes times their scales.  The fast kernel's fp16 V already holds codes times scales; the
+// bf16 redo kernel reads the staged bf16 V codes and multiplies each probability by its
+// key's V scale before the PV product (the row sum takes the probabilities alone).  Scales
+// of a tile come into LDS with its V loads (wave 0 the K scales, wave 1 the V scales).
 template <int D, int WAVES, bool F16, bool F8>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnArgs a, const PfItem* __restrict__ items,
                                                                             int32_t n_items, int32_t* __restrict__ wide) {
-  static_assert(!(F16 && F8), "fp8 pools run the bf16-V kernel");
   using C = PrefillCfg<D>;
   constexpr int ROWS = 32 * WAVES;
   constexpr int NT = 64 * WAVES;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   const int32_t per_xcd = (total + 7) / 8;
   const int32_t lin = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
   if (lin >= total) return;
-  if constexpr (!F16 && !F8) {
+  if constexpr (!F16) {
     if (__builtin_amdgcn_readfirstlane(wide[lin]) == 0) return;   // the fast kernel's output stands
   }
   const int hkv = lin / n_items;
@@ -241,10 +242,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   // Block ids of a full tile (4 consecutive table entries, wave-uniform) are fetched one
   // iteration before they are needed, so no load waits on a table lookup; only the last,
   // partial tile computes clamped per-lane keys.
+  // Staged copies (the fp16 V copy; on fp8 pools also the bf16 codes and the scales): the
+  // staged blocks of this request are consecutive, block k/16 of the request at staged block
+  // stage0 + k/16 (stage0 = its first staged block minus the first block it holds), and every
+  // tile's four blocks are staged (zeros past seq_len), so whole tiles are read.
+  const int32_t stage0 = (F16 || F8) ? __builtin_amdgcn_readfirstlane(a.req[r_id].stage) -
+                                           v16_first_block(a.window, t, L)
+                                     : 0;
+  // block holding key 16e of the request: a table entry, or (fp8 pools) a staged block
+  auto entry_blk = [&](int32_t e) -> int32_t { return F8 ? stage0 + e : table_row[e]; };
   struct Blocks { int32_t b0, b1, b2, b3; };
   auto fetch_blocks = [&](int32_t j) -> Blocks {
     j += t0;
     if (j * kBK + kBK > kend) return Blocks{0, 0, 0, 0};     // partial tile: not used
+    if constexpr (F8) {
+      const int32_t e0 = stage0 + 4 * j;
+      if constexpr (F16) return Blocks{e0 + (w >> 2), e0 + (w >> 2) + 2, 0, 0};
+      return Blocks{e0, e0 + 1, e0 + 2, e0 + 3};
+    }
     // through the constant address space, so the compiler reads the (wave-uniform) entries
     // with a scalar load, which does not wait behind the tile loads in flight
     const __attribute__((address_space(4))) int32_t* e =
@@ -276,23 +291,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
         const int32_t kg = min(j * kBK + 4 * (w + WAVES * u) + (lane >> 4), kend - 1);
-        const int64_t off = ((int64_t)table_row[kg >> 4] * kBlk + (kg & 15)) * row_elems + 8 * chunk_sw;
+        const int64_t off = ((int64_t)entry_blk(kg >> 4) * kBlk + (kg & 15)) * row_elems + 8 * chunk_sw;
         load_lds16(base + off, dst + (w + WAVES * u) * 1024);
       }
     }
   };
   auto issue_k = [&](int32_t j, const Blocks& bl, unsigned char* dst) { issue(kc, j, bl, dst); };
   // F16: V from the transposed fp16 copy ([staged block][Hkv][D][16 keys in kperm order]).
-  // The staged blocks of this request are consecutive, block k/16 of the request at staged
-  // block stage0 + k/16 (stage0 = its first staged block minus the first block it holds),
-  // and every tile's four blocks are staged (zeros past seq_len), so whole tiles are read.
   // In LDS a V tile is four 4 KB blocks of 128 dim rows x 32 bytes; the two 16-byte halves
   // of row d are swapped when bit 3 of d is set, which spreads a wave's operand reads (16
   // consecutive dims, one half) over all banks.  Load instruction u of wave w fills the 1 KB
   // piece I = w + WAVES*u: block I/4, dims 32(I%4) .. +31; lane l takes dim 32(I%4) + l/2,
   // half (l%2) ^ (bit 3 of the dim).
   static_assert(WAVES % 4 == 0, "a wave's V pieces share one dim range");
-  const int32_t stage0 = F16 ? __builtin_amdgcn_readfirstlane(a.req[r_id].stage) - v16_first_block(a.window, t, L) : 0;
   const uint16_t* v16 = F16 ? (const uint16_t*)a.v_staged + (int64_t)stage0 * blk_stride + (int64_t)hkv * D * kBlk : nullptr;
   const uint64_t v16_b = (uint64_t)(uintptr_t)v16;
   const uint32_t v16_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v16_b);
@@ -311,20 +322,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       issue(vc, j, bl, dst);
     }
   };
-  // F8: the 64 K scales (wave 0) and V scales (wave 1) of tile j, one per lane, into the ring
-  // slot at dst (K scales at +0, V scales at +256); staged layout [block][2][Hkv][16]
-  auto issue_sc = [&](int32_t j, const Blocks& bl, unsigned char* dst) {
+  // F8: the 64 K scales (wave 0) and, for the bf16 kernel, V scales (wave 1) of tile j, one
+  // per lane, into the ring slot at dst (K scales at +0, V scales at +256); staged layout
+  // [staged block][2][Hkv][16]
+  auto issue_sc = [&](int32_t j, const Blocks&, unsigned char* dst) {
     if constexpr (F8) {
-      if (w >= 2) return;
+      if (w >= (F16 ? 1 : 2)) return;
       j += t0;
-      int32_t kg = j * kBK + lane, blk;
-      if (j * kBK + kBK <= kend) {
-        const int bi = lane >> 4;
-        blk = bi == 0 ? bl.b0 : bi == 1 ? bl.b1 : bi == 2 ? bl.b2 : bl.b3;
-      } else {
-        kg = min(kg, kend - 1);
-        blk = table_row[kg >> 4];
-      }
+      const int32_t kg = min(j * kBK + lane, kend - 1);        // (the last tile: clamped keys)
+      const int32_t blk = stage0 + (kg >> 4);
       load_lds4(a.k_scale + (((int64_t)blk * 2 + w) * a.Hkv + hkv) * 16 + (kg & 15), dst + 256 * w);
     }
   };
@@ -568,9 +574,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
     for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        // F8: the V scales of this group's eight keys (two 4-key runs)
+        // F8, bf16 kernel: the V scales of this group's eight keys (two 4-key runs)
         f32x4 vsc[2];
-        if constexpr (F8) {
+        if constexpr (F8 && !F16) {
 #pragma unroll
           for (int hq = 0; hq < 2; ++hq)
             vsc[hq] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(
@@ -684,7 +690,12 @@ hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipSt
   int32_t* wide = (int32_t*)((char*)ws + p.off_pf_wide);     // zeroed by the plan kernel
   const int64_t total = p.n_pf * p.Hkv;
   const dim3 grid((unsigned)((total + 7) / 8 * 8));
-  if (p.f8) {   // the staged copy of fp8 pools (launched by launch_stage_fp8)
+  if (p.f8) {   // the staged copies of fp8 pools (launched by launch_stage_fp8)
+    hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, true, true>), grid, dim3(64 * kWaves), 0, s, a, items,
+                       (int32_t)p.n_pf, wide);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // items whose dequantized V left fp16's range (normally none: these workgroups exit at once)
     hipLaunchKernelGGL((prefill_tile_mfma<128, kWaves, false, true>), grid, dim3(64 * kWaves), 0, s, a, items,
                        (int32_t)p.n_pf, wide);
     return hipGetLastError();

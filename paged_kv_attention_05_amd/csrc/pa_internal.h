@@ -55,18 +55,17 @@ struct Plan {
   int32_t pf_tokens;               // 0: prefill path off
   int32_t decode_kind;             // 0: vector kernel, 1: bf16 matrix-core kernel
   int32_t window;                  // sliding window in tokens (0: none)
-  int32_t f8;                      // 1: fp8 pools (prefill requests read a staged bf16 copy)
-  int32_t v16;                     // 1: bf16 pools whose prefill requests read V from a staged
-                                   //    fp16 copy
-  int32_t stage_w;                 // f8: width of the staged block table (blocks per request)
+  int32_t f8;                      // 1: fp8 pools (prefill requests read staged bf16 K codes)
+  int32_t v16;                     // 1: prefill requests read V from a staged fp16 copy (bf16
+                                   //    pools: V converted; fp8 pools: the codes times their scales)
   int32_t graph_max;               // > 0: the call is sized for every seq_len = graph_max (the
                                    //      planner counts device lengths clamped to it)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed); n_small counts tile-splits
   int64_t n_g1, n_g3;              // matrix-core small kernels: single-tile and grouped items
-  int64_t n_stage;                 // f8: staged blocks (all blocks of the prefill requests)
+  int64_t n_stage;                 // staged blocks of the prefill requests
   // workspace layout (byte offsets)
   size_t off_req, off_small, off_merge, off_pf, off_pf_wide, off_pm, off_pl, off_pacc, off_g1, off_g3;
-  size_t off_f8_tab, off_f8_k, off_f8_v, off_f8_s, off_v16, total_bytes;
+  size_t off_f8_k, off_f8_v, off_f8_s, off_v16, total_bytes;
 };
 
 struct alignas(16) SmallItem {
@@ -86,7 +85,7 @@ struct alignas(8) PfItem {
 // per-request offsets written by the planner (exclusive scans)
 struct alignas(16) ReqOffsets {
   int32_t small, merge, pf, nsplit;
-  int32_t stage;                       // first staged block of the request (fp8 pools)
+  int32_t stage;                       // first staged block of the request
   int32_t g1, g3;                      // offsets in the matrix-core small kernels' two item lists
   int32_t pad0;
 };
@@ -128,14 +127,13 @@ __host__ __device__ __forceinline__ int32_t v16_first_block(int32_t window, int3
 // prefill kernel's P^T fragments hold their keys, so that a lane's 8 keys of one dim are
 // one 16-byte read.
 __host__ __device__ __forceinline__ int kperm(int q) { return (q & 3) | ((q & 4) << 1) | ((q & 8) >> 1); }
-// Staged blocks of request r: every block of a prefill-path request (fp8 pools), or, for
-// the fp16 V copy of bf16 pools, the blocks of every 64-key tile from v16_first_block on
-// (the last tile's blocks past the request's end are staged as zeros).
+// Staged blocks of a prefill-path request: the blocks of every 64-key tile from
+// v16_first_block on (the last tile's blocks past the request's end are staged as zeros), for
+// the fp16 V copy and, on fp8 pools, the bf16 copies of the codes and the scales.  Block j of
+// the request is staged block req.stage + j - v16_first_block.
 __host__ __device__ __forceinline__ int32_t staged_blocks(const Plan& p, int32_t t, int32_t L) {
-  if (!use_prefill_path(p, t, L)) return 0;
-  if (p.f8) return (L + p.bs - 1) / p.bs;
-  if (p.v16) return 4 * ((L + 63) / 64) - v16_first_block(p.window, t, L);
-  return 0;
+  if (!use_prefill_path(p, t, L) || !p.v16) return 0;
+  return 4 * ((L + 63) / 64) - v16_first_block(p.window, t, L);
 }
 // Keys one small tile of a request with context L can see: all L, or with a sliding window
 // of w tokens at most w + tile_tokens - 1 (the tile's rows are consecutive), plus up to 63
@@ -218,9 +216,11 @@ struct AttnArgs {
   // fp8 pools: float32 scales [num_slots, Hkv] of K and V (null: the pools hold q's dtype)
   const float* k_scale;
   const float* v_scale;
-  // bf16 pools with the staged V: the transposed fp16 copy [staged block][Hkv][D][16] of the
-  // prefill requests' blocks (request r's block j at staged block req[r].stage + j - first,
-  // first = v16_first_block; within a row, position q holds key kperm(q))
+  // prefill requests: the transposed fp16 copy [staged block][Hkv][D][16] of their V blocks
+  // (request r's block j at staged block req[r].stage + j - first, first = v16_first_block;
+  // within a row, position q holds key kperm(q)).  On fp8 pools k_cache / v_cache / k_scale
+  // of the prefill kernels point at the staged bf16 codes [staged block][16][Hkv][D] and
+  // the staged scales, at the same staged block numbers.
   const void* v_staged;
   const ReqOffsets* req;
 };
@@ -248,8 +248,8 @@ hipError_t launch_prefill_mfma(const Plan& p, const AttnArgs& a, void* ws, hipSt
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t s);
 hipError_t launch_mfma_probe(int32_t iters, int32_t data, uint32_t* sink, int32_t grid, hipStream_t s);
 int64_t mfma_probe_flops(int32_t iters, int32_t grid);
-// fp8 pools: stage the prefill requests' blocks as bf16 codes and scaled scales, then run the
-// prefill kernel on the staged copy
+// fp8 pools: stage the prefill requests' blocks (bf16 codes, scales, the fp16 V copy), then
+// run the prefill kernels on them
 hipError_t launch_stage_fp8(const Plan& p, const AttnArgs& a, float scale_abs_log2e, void* ws, hipStream_t s);
 // bf16 pools: copy the prefill requests' V blocks to fp16 (flagging, for the bf16 prefill
 // kernel, the items whose V leaves fp16's range)

@@ -62,7 +62,7 @@ Plan make_plan(int32_t g, int32_t window, int32_t f8, int32_t split, int32_t M) 
   p.decode_kind = 1;
   p.window = window;
   p.f8 = f8;
-  p.v16 = (!f8 && p.pf_tokens > 0) ? 1 : 0;
+  p.v16 = p.pf_tokens > 0 ? 1 : 0;
   p.graph_max = M;
   return p;
 }

@@ -10,8 +10,9 @@
 //     past a request's last block are never read ("Attention over the pool" of "Engine v2:
 //     one core for every request"), whether full tiles (entries 4j .. 4j+3, one tile ahead)
 //     or the last, partial tile (keys clamped to kend - 1);
-//   - K/V pool rows, the staged fp16 V rows (stage0 + 4(j + t0) + block), the staged fp8
-//     copy, its table and scales, q and out rows are inside their buffers;
+//   - K/V pool rows, the staged fp16 V rows (stage0 + 4(j + t0) + block), the staged bf16
+//     codes and scales of fp8 pools (staged blocks of the request itself), q and out rows
+//     are inside their buffers;
 //   - ring slot i % 3 and the LDS destinations stay inside the kernel's shared memory.
 // The pool block ids themselves come from the batch (every parity batch's tables hold valid
 // ids); they are checked too.
@@ -81,13 +82,12 @@ void check_batch(const BatchIn& B) {
   p.decode_kind = 1;
   p.window = B.window;
   p.f8 = B.f8;
-  p.v16 = B.f8 ? 0 : 1;
+  p.v16 = 1;
 
   // ---- the planner: per-request offsets (exclusive scans) and the prefill items
   struct Req { int32_t pf, stage; };
   std::vector<Req> req(B.R + 1);
   std::vector<std::pair<int32_t, int32_t>> items;           // (r, tok0)
-  int32_t stage_w = 0;
   int64_t n_stage = 0;
   for (int32_t r = 0; r < B.R; ++r) {
     const int32_t t = B.qsl[r + 1] - B.qsl[r], L = B.lens[r];
@@ -98,7 +98,6 @@ void check_batch(const BatchIn& B) {
     const int32_t tiles = npf > 0 ? (t + p.pf_tokens - 1) / p.pf_tokens : 0;
     for (int32_t li = 0; li < npf; ++li) items.push_back({r, (tiles - 1 - li) * p.pf_tokens});
     n_stage += st;
-    stage_w = std::max(stage_w, st);
   }
   req[B.R] = Req{(int32_t)items.size(), (int32_t)n_stage};
   const int64_t n_items = (int64_t)items.size();
@@ -110,9 +109,9 @@ void check_batch(const BatchIn& B) {
   const int64_t qo_elems = B.N * B.H * B.D;
   auto nblocks_of = [&](int32_t r) { return (B.lens[r] + kBlk - 1) / kBlk; };
 
-  // ---- staging kernels: one workgroup per staged block
-  std::vector<int32_t> stab;                                 // fp8: the staged table [R][stage_w]
-  if (B.f8) stab.assign((size_t)B.R * std::max(stage_w, 1), -1);
+  // ---- staging kernels (stage_v16, or stage_fp8 on fp8 pools): one workgroup per staged
+  // block, request r's block j at staged block req[r].stage + j - first
+  const int64_t row_elems_s = (int64_t)B.Hkv * B.D;
   for (int64_t sb = 0; sb < n_stage; ++sb) {
     int lo = 0, hi = B.R - 1;                                // owner: largest r with stage <= sb
     while (lo < hi) {
@@ -122,34 +121,37 @@ void check_batch(const BatchIn& B) {
     }
     const int32_t r = lo, t = B.qsl[r + 1] - B.qsl[r], L = B.lens[r];
     expect(sb - req[r].stage < req[r + 1].stage - req[r].stage, "staged block owner", sb, r);
-    if (B.f8) {
-      const int32_t j = (int32_t)(sb - req[r].stage);
-      expect(j < nblocks_of(r) && j < B.stride, "fp8 staging: table entry", r, j);
-      expect(j < stage_w, "fp8 staging: staged table column", r, j, stage_w);
-      if (j < stage_w) stab[(size_t)r * stage_w + j] = (int32_t)sb;
+    const int32_t j = (int32_t)(sb - req[r].stage) + pa::v16_first_block(B.window, t, L);
+    const int32_t nkeys = std::min(16, L - 16 * j);
+    if (nkeys > 0) {
+      expect(j < nblocks_of(r) && j < B.stride && j >= 0, "staging: table entry", r, j);
       const int32_t src = B.table[(size_t)r * B.stride + j];
-      in_range((int64_t)src * blk_stride, blk_stride, pool_elems, "fp8 staging: pool block");
-    } else {
-      const int32_t j = (int32_t)(sb - req[r].stage) + pa::v16_first_block(B.window, t, L);
-      const int32_t nkeys = std::min(16, L - 16 * j);
-      if (nkeys > 0) {
-        expect(j < nblocks_of(r) && j < B.stride && j >= 0, "v16 staging: table entry", r, j);
-        const int32_t src = B.table[(size_t)r * B.stride + j];
+      for (int lk = 0; lk < nkeys; ++lk)
+        in_range(((int64_t)src * 16 + lk) * row_elems_s, row_elems_s, pool_elems, "staging: pool row");
+      if (B.f8)
         for (int lk = 0; lk < nkeys; ++lk)
-          in_range(((int64_t)src * 16 + lk) * row_elems, row_elems, pool_elems, "v16 staging: V row");
-      }
-      for (int head = 0; head < B.Hkv; ++head)
-        for (int tid = 0; tid < 256; ++tid) {
-          const int od = tid >> 1, oh = tid & 1;
-          in_range((((int64_t)sb * B.Hkv + head) * B.D + od) * 16 + 8 * oh, 8, n_stage * blk_stride,
-                   "v16 staging: staged row");
-        }
-      for (int32_t it = req[r].pf; it < req[r + 1].pf; ++it)
-        in_range((int64_t)(B.Hkv - 1) * n_items + it, 1, n_items * B.Hkv, "v16 staging: range flag");
+          in_range(((int64_t)src * 16 + lk) * B.Hkv, B.Hkv, (int64_t)(B.num_blocks + 1) * 16 * B.Hkv,
+                   "fp8 staging: scale of a pool slot");
     }
+    for (int head = 0; head < B.Hkv; ++head) {
+      for (int tid = 0; tid < 256; ++tid) {
+        const int od = tid >> 1, oh = tid & 1, lk = tid >> 4, lc = tid & 15;
+        in_range((((int64_t)sb * B.Hkv + head) * B.D + od) * 16 + 8 * oh, 8, n_stage * blk_stride,
+                 "staging: transposed fp16 V row");
+        if (B.f8)
+          in_range(((int64_t)sb * 16 + lk) * row_elems_s + (int64_t)head * B.D + 8 * lc, 8, n_stage * blk_stride,
+                   "fp8 staging: bf16 code row");
+      }
+      if (B.f8)
+        for (int x = 0; x < 32; ++x)
+          in_range((((int64_t)sb * 2 + (x >> 4)) * B.Hkv + head) * 16 + (x & 15), 1, n_stage * 2 * B.Hkv * 16,
+                   "fp8 staging: staged scale");
+    }
+    for (int32_t it = req[r].pf; it < req[r + 1].pf; ++it)
+      in_range((int64_t)(B.Hkv - 1) * n_items + it, 1, n_items * B.Hkv, "staging: range flag");
   }
 
-  // ---- the prefill kernels: fp16 (bf16 pools) plus the bf16 redo kernel, or the fp8 kernel
+  // ---- the prefill kernels: the fp16 kernel and the bf16 redo kernel of the pool kind
   const int TILE = kBK * 2 * B.D, V_RING = 0, K_RING = V_RING + kNBuf * TILE;
   const int SC_RING = K_RING + kNBuf * TILE, SC_TILE = B.f8 ? 2 * kBK * 4 : 0;
   const int SMEM = std::max(SC_RING + kNBuf * SC_TILE, kRows * 2 * B.D);
@@ -171,16 +173,23 @@ void check_batch(const BatchIn& B) {
     const int32_t t0 = B.window > 0 ? std::max(0, c + tok0 - B.window + 1) / kBK : 0;
     const int32_t ntiles = (kend + kBK - 1) / kBK - t0;
     expect(ntiles >= 1, "item has a tile", r, tok0, ntiles);
-    const int32_t* trow = B.f8 ? &stab[(size_t)r * stage_w] : &B.table[(size_t)r * B.stride];
-    const int32_t tw = B.f8 ? stage_w : B.stride;           // the table the kernel reads
+    const int32_t* trow = &B.table[(size_t)r * B.stride];
     const int32_t tvalid = nblocks_of(r);                    // entries of the request
+    // K (and the redo kernel's V): pool rows through the table, or (fp8 pools) the staged
+    // bf16 code rows at staged block numbers
     const int64_t kv_elems = B.f8 ? n_stage * blk_stride : pool_elems;
-    const int32_t stage0 = B.f8 ? 0 : req[r].stage - pa::v16_first_block(B.window, t, L);
+    const int32_t stage0 = req[r].stage - pa::v16_first_block(B.window, t, L);
     auto entry = [&](int32_t e, const char* what) -> int32_t {
-      expect(e >= 0 && e < tvalid && e < tw, what, r, e, tvalid);
-      if (e < 0 || e >= tw) return 0;
+      expect(e >= 0 && e < tvalid, what, r, e, tvalid);
+      if (B.f8) {
+        const int32_t sb = stage0 + e;                       // one of the request's staged blocks
+        expect(sb >= req[r].stage && sb < req[r + 1].stage, "staged block of the request", r, sb);
+        return sb;
+      }
+      expect(e < B.stride, what, r, e, B.stride);
+      if (e < 0 || e >= B.stride) return 0;
       const int32_t blk = trow[e];
-      expect(B.f8 ? (blk >= 0 && blk < n_stage) : (blk >= 0 && blk <= B.num_blocks), "block id", r, e, blk);
+      expect(blk >= 0 && blk <= B.num_blocks, "block id", r, e, blk);
       return blk;
     };
     // the block ids fetched one tile ahead: fetch_blocks(j) for j up to ntiles + 4
@@ -220,8 +229,8 @@ void check_batch(const BatchIn& B) {
               koff = ((int64_t)entry(kg >> 4, "partial-tile table entry") * kBlk + (kg & 15)) * row_elems +
                      8 * chunk_sw;
             }
-            in_range((int64_t)hkv * B.D + koff, 8, kv_elems, "K row (and V row of the bf16 kernels)");
-            if (!B.f8) {
+            in_range((int64_t)hkv * B.D + koff, 8, kv_elems, "K row (and V row of the bf16 redo kernel)");
+            {
               // the fp16 kernel's V: staged block stage0 + 4j + piece / 4
               const int64_t sb = (int64_t)stage0 + 4 * j + (piece >> 2);
               expect(sb >= req[r].stage && sb < req[r + 1].stage, "staged V block of the request", r, sb);
@@ -229,14 +238,9 @@ void check_batch(const BatchIn& B) {
                        "staged V row");
             }
           }
-          if (B.f8 && w < 2) {                               // scales: wave 0 K, wave 1 V
-            int32_t kg = j * kBK + lane, blk;
-            if (full) {
-              blk = entry(4 * j + (lane >> 4), "scale table entry");
-            } else {
-              kg = std::min(kg, kend - 1);
-              blk = entry(kg >> 4, "scale table entry");
-            }
+          if (B.f8 && w < 2) {                               // scales: wave 0 K, wave 1 V (redo)
+            const int32_t kg = std::min(j * kBK + lane, kend - 1);
+            const int32_t blk = entry(kg >> 4, "scale block");
             in_range((((int64_t)blk * 2 + w) * B.Hkv + hkv) * 16 + (kg & 15), 1, n_stage * 2 * B.Hkv * 16,
                      "staged scale");
             in_range(SC_RING + slot * SC_TILE + 256 * w + 4 * lane, 4, SMEM, "scale ring slot");

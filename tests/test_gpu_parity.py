@@ -266,6 +266,24 @@ def _fp8_step(b, window=0):
     return out.float().cpu().numpy(), ref64
 
 
+def test_fp8_prefill_v_beyond_fp16_range():
+    """fp8 pools whose dequantized V passes fp16's largest finite value (65504) in a few
+    slots of one request (context and new tokens): that request's prefill items are redone
+    by the bf16 kernel, the other request's stay on the fp16 kernel; both within the bound."""
+    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=37)
+    r0 = b.requests[0]
+    pool_v = b.v_cache.view(-1, b.num_kv_heads, b.head_dim)
+    for pos, hk, d, val in [(7, 0, 3, 1.0e5), (260, 5, 100, -2.5e5), (431, 7, 64, 7.0e4)]:
+        pool_v[workloads.slot_of(r0.blocks, pos, b.block_size), hk, d] = val
+    b.v[3, 2, 5] = 9.0e4                 # row 3 of request 0 (position 503)
+    got, ref64 = _fp8_step(b)
+    err = attention_error(got, ref64, "bf16")
+    H.log(f"[parity] fp8 prefill with V beyond fp16: error {err:.3g} x bound")
+    H.record({"case": "fp8_prefill_wide_v", "dtype": "bf16", "kv": "fp8_e4m3", "error_x_bound": err})
+    assert err <= 1.0, err
+
+
 @pytest.mark.parametrize("scale", [-0.11, 0.0])
 def test_negative_and_zero_scale_every_path(scale):
     """A negative softmax scale (applied as |scale| on -q) and a zero scale (uniform weights
