@@ -160,6 +160,45 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   int32_t split = 64;
   while (split < 2048 && (double)split * 2 <= target) split *= 2;
   while (split < 2048 && (int64_t)split * 8 < span_max) split *= 2;
+  // Whole waves of workgroups: when the small tiles' workgroups would not fill the GPU once
+  // (about four run per CU at a time), a shorter split (any multiple of 64 keys, down to a
+  // quarter, at most 16 per tile) can make them fill it: the split with the fewest
+  // (waves of workgroups) x (keys per split) wins.
+  {
+    auto small_wgs = [&](int32_t s) {
+      pa::Plan q = p;
+      q.split_keys = s;
+      int64_t n = 0;
+      for (int32_t r = 0; r < R; ++r) {
+        int32_t a, b, c, d;
+        const int32_t t = qsl[r + 1] - qsl[r];
+        if (q.decode_kind == 1) {
+          pa::small_groups(q, t, len_of(r), &a, &b);
+          n += a + b;
+        } else {
+          pa::request_counts(q, t, len_of(r), &a, &b, &c, &d);
+          n += a;
+        }
+      }
+      return n * Hkv;
+    };
+    constexpr int64_t kConcurrentWGs = 4 * 256;
+    const int64_t n0 = small_wgs(split);
+    if (n0 > 0 && n0 < kConcurrentWGs) {
+      int64_t best_cost = ((n0 + kConcurrentWGs - 1) / kConcurrentWGs) * (int64_t)split;
+      int32_t best = split;
+      for (int32_t s = split - 64; s >= std::max(64, split / 4); s -= 64) {
+        if ((span_max + s - 1) / s > 16) break;
+        const int64_t n = small_wgs(s);
+        const int64_t cost = ((n + kConcurrentWGs - 1) / kConcurrentWGs) * (int64_t)s;
+        if (cost < best_cost) {
+          best_cost = cost;
+          best = s;
+        }
+      }
+      split = best;
+    }
+  }
   p.split_keys = split;
 
   int64_t ns = 0, nm = 0, np = 0, ng = 0, n1 = 0, n3 = 0;
