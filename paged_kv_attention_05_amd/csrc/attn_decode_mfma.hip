@@ -78,8 +78,12 @@ __device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// (nontemporal: the rows are streamed rather than kept in the caches; the cache-policy
+// operand 2 is the instruction's nt bit.  Measured against cached loads: 256 decodes 5.72 ->
+// 6.23 TB/s, speculative verification 4.72 -> 5.20, the long-context decodes 5.63 -> 6.22,
+// even the shared-prefix decodes, which re-read the prefix blocks, 4.43 -> 5.16.)
 __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 2);
 }
 
 // v of lane i of the lane's quad, for i = 0..3 (DPP quad permutes)
@@ -220,6 +224,8 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
   // V: row lane/4, quarter lane%4 of the row.  Scales: K and V scale of key 4G + n%4 (the
   // lane's quad broadcasts them to the four keys of its S^T rows).  Every load is an
   // ordinary vector load, so the compiler waits for exactly the block it is about to use.
+  // (Unlike the bf16 rows, these stay cached loads: nontemporal ones measured slower here,
+  // 6% on 256 decodes and 27% on speculative verification, whose tiles re-read each block.)
   constexpr int VX = D / 64;                                   // 16-byte pieces of V codes per lane
   constexpr int KX = D / 64;                                   // 16-byte pieces of K codes per lane
   struct Blk { u32x4 k[KX]; u32x4 v[VX]; float ks, vs; };
