@@ -270,13 +270,8 @@ def test_fp8_prefill_v_beyond_fp16_range():
     """fp8 pools whose dequantized V passes fp16's largest finite value (65504) in a few
     slots of one request (context and new tokens): that request's prefill items are redone
     by the bf16 kernel, the other request's stay on the fp16 kernel; both within the bound."""
-    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
-                              head_dim=128, seed=37)
-    r0 = b.requests[0]
-    pool_v = b.v_cache.view(-1, b.num_kv_heads, b.head_dim)
-    for pos, hk, d, val in [(7, 0, 3, 1.0e5), (260, 5, 100, -2.5e5), (431, 7, 64, 7.0e4)]:
-        pool_v[workloads.slot_of(r0.blocks, pos, b.block_size), hk, d] = val
-    b.v[3, 2, 5] = 9.0e4                 # row 3 of request 0 (position 503)
+    b = _plant_wide_v(workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32,
+                                            num_kv_heads=8, head_dim=128, seed=37))
     got, ref64 = _fp8_step(b)
     err = attention_error(got, ref64, "bf16")
     H.log(f"[parity] fp8 prefill with V beyond fp16: error {err:.3g} x bound")
@@ -560,17 +555,28 @@ def test_long_context_full_size_window():
     H.check_batch(b, row_mask=_sample_rows(b, 6), label="long_context_window_4096", window=4096)
 
 
-def _wide_v_batch():
-    """Two prefill chunks; request 0 has V values past fp16's largest finite value (65504) in
-    three context slots and in one of its new tokens."""
-    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
-                              head_dim=128, seed=31)
+def _plant_wide_v(b):
+    """Request 0 of b gets V values past fp16's largest finite value (65504) in three context
+    slots and in one of its new tokens.  The K rows of those (slot, KV head) pairs are zeroed,
+    so every row gives them a small weight: the outputs stay of ordinary size, where the bf16
+    bound measures the arithmetic rather than the rounding of a 10^5-sized output, while the
+    whole request still has to take the redo path (an fp16 V would hold infinities)."""
     r0 = b.requests[0]
+    pool_k = b.k_cache.view(-1, b.num_kv_heads, b.head_dim)
     pool_v = b.v_cache.view(-1, b.num_kv_heads, b.head_dim)
     for pos, hk, d, val in [(7, 0, 3, 1.0e5), (260, 5, 100, -2.5e5), (431, 7, 64, 7.0e4)]:
-        pool_v[workloads.slot_of(r0.blocks, pos, b.block_size), hk, d] = val
+        slot = workloads.slot_of(r0.blocks, pos, b.block_size)
+        pool_v[slot, hk, d] = val
+        pool_k[slot, hk, :] = 0.0
     b.v[3, 2, 5] = 9.0e4                 # row 3 of request 0 (position 503)
+    b.k[3, 2, :] = 0.0
     return b
+
+
+def _wide_v_batch():
+    """Two prefill chunks, request 0 with V beyond fp16's range (_plant_wide_v)."""
+    return _plant_wide_v(workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32,
+                                               num_kv_heads=8, head_dim=128, seed=31))
 
 
 def test_prefill_v_beyond_fp16_range():
