@@ -1,4 +1,4 @@
-// Prefill-chunk paged attention on bf16 matrix cores.
+// Prefill-chunk paged attention on the matrix cores.
 //
 // A request whose rows times grouped heads exceed 16 query columns (a prefill chunk) is cut
 // into tiles of 32 * WAVES query rows: (32 * WAVES) / g consecutive tokens times the g query
@@ -6,43 +6,49 @@
 // on chip serves all g heads (grouped-query attention without repeating K/V, as the
 // vllm-lite README's fold does for its CPU path).  The causal mask is offset by the request's
 // computed tokens: row i of a request with seq_len L and t rows sits at position L - t + i
-// ("Attention over the pool" in "Engine v2: one core for every request").  K/V are read in
-// place through the block table, 64 keys (four 16-token blocks) at a time; the online
-// softmax keeps exact attention without a score matrix in memory (the FlashAttention section
-// of the tensorsofthewall.com post).
+// ("Attention over the pool" in "Engine v2: one core for every request").  Keys come 64
+// (four 16-token blocks) at a time; the online softmax keeps exact attention without a score
+// matrix in memory (the FlashAttention section of the tensorsofthewall.com post).
 //
 // Data movement: each 64-key K and V tile goes from HBM straight into LDS with the gfx950
 // direct loads (global_load_lds_dwordx4, 16 bytes per lane, no register staging), into rings
 // of three tiles, so later tiles stream in while the current one is computed.  A load's
-// block address (base + block id x block bytes) is formed on the scalar unit from the
-// wave's own two block-table entries per tile.  K comes from
-// the pool through the block table; V from an fp16 copy of the request's blocks made just
-// before (v16_stage.hip).  An LDS row is
-// one key's 256 bytes; its sixteen 16-byte chunks are stored XOR-swizzled (chunk c of row r
-// at slot c ^ f(r), f(r) = 4*(r%4) + (r/4)%4), which makes both the K reads (16 consecutive
-// rows, one chunk) and the V transpose reads (4 rows x 4 chunks) free of bank conflicts.
+// block address (base + block number x block bytes) is formed on the scalar unit.
+//   - bf16 pools: K is read in place, through the wave's two block-table entries per tile;
+//     V from the fp16 copy of the request's blocks that stage_v16 (v16_stage.hip) made just
+//     before, at staged block numbers.
+//   - fp8 pools: stage_fp8 (fp8_stage.hip) made bf16 copies of the K (and V) codes, their
+//     scales, and an fp16 copy of V dequantized; all are read at staged block numbers.
+// An LDS row of K is one key's 256 bytes; its sixteen 16-byte chunks are stored XOR-swizzled
+// (chunk c of row r at slot c ^ f(r), f(r) = 4*(r%4) + (r/4)%4), which makes the K reads (16
+// consecutive rows, one chunk) and the bf16 kernels' V transpose reads (4 rows x 4 chunks)
+// free of bank conflicts.
 //
 // Compute: wave w owns tile rows 32w .. 32w+31, one row per lane column.
 //   S^T[key][row] = K[key][:] . Q[row][:]     mfma_f32_32x32x16_bf16, K from LDS (A operand,
 //                                             one 16-byte read per lane), Q^T in registers.
-//   O^T[d][row]  += V^T[d][key] P^T[key][row]  mfma_f32_32x32x16_f16; P^T is the S^T
-//                                             accumulator layout with the key index
-//                                             bit-permuted (bits 2 and 3 swapped in each
-//                                             16-key chunk); V^T comes from LDS with the same
-//                                             permutation through two ds_read_tr16_b64.
+//   O^T[d][row]  += V^T[d][key] P^T[key][row]  mfma_f32_32x32x16_f16 (the fp16 kernels); P^T
+//                                             is the S^T accumulator layout with the key
+//                                             index bit-permuted (bits 2 and 3 swapped in
+//                                             each 16-key chunk), and the staged fp16 copy
+//                                             holds V^T in that order, so a lane's operand is
+//                                             one 16-byte read.  The bf16 kernels read V^T
+//                                             from key rows with two ds_read_tr16_b64.
 // Two groups of four waves run in ping-pong (one wave of each per SIMD), so one wave's
 // exponentials overlap the other's matrix products (see the loop below).
 // Softmax per row in base 2: one FMA and one v_exp_f32 per score; the running max is only
 // moved (and O rescaled) when a row's max grows by more than 8 (a factor 256), so rescaling
 // is rare; the sum uses the same reference, so the result is exact either way.
 //
-// Precision of PV: V is converted from bf16 to fp16 (by the staging kernel), which is exact
-// for |v| <= 65504, and P is rounded to nearest fp16 (p <= 256 here), with the row sum taken
-// over the same rounded values.  The output is then an exact convex combination of V rows whose
-// weights are off by at most 2^-12 relative: a single bf16 P (2^-9) would use most of the
-// 2e-2 budget against ~10x outlier values.  An item that meets |v| > 65504 is redone by a
-// second kernel that keeps V in bf16 and carries P as a bf16 pair (truncated high part plus
-// the bf16 rounding of the remainder, two products per chunk, ~16 significant bits).
+// Precision of PV: in the fp16 kernels V is fp16 (bf16 pools: converted, exact for
+// 2^-14 <= |v| <= 65504 and off by at most 2^-25 below; fp8 pools: code times scale, off by
+// at most 2^-11 relative), and P is rounded to nearest fp16 (p <= 256 here), with the row sum
+// taken over the same rounded values.  The output is then a convex combination of V rows
+// whose weights are off by at most 2^-12 relative: a single bf16 P (2^-9) would use most of
+// the 2e-2 budget against ~10x outlier values.  An item that meets |v| > 65504 is redone by
+// the bf16 kernel of its pool kind, which keeps V in bf16 and carries P as a bf16 pair
+// (truncated high part plus the bf16 rounding of the remainder, two products per chunk,
+// ~16 significant bits).
 #include <type_traits>
 
 #include "pa_internal.h"

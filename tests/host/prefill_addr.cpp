@@ -1,7 +1,7 @@
 // Host replica of the prefill path's address arithmetic, checked against the allocations.
 //
-// The prefill kernels (attn_prefill_mfma.hip: the fp16 kernel, the bf16 redo kernel and the
-// fp8 kernel) and their staging kernels (v16_stage.hip, fp8_stage.hip) compute every global
+// The prefill kernels (attn_prefill_mfma.hip: the fp16 kernel and the bf16 redo kernel, for
+// bf16 and for fp8 pools) and their staging kernels (v16_stage.hip, fp8_stage.hip) compute every global
 // address from the planner's items and the batch layout.  This program redoes that
 // arithmetic on the host, lane by lane, for every workgroup of every launch a batch makes,
 // and checks each access against its buffer:
