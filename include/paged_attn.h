@@ -152,8 +152,10 @@ size_t paged_attention_workspace_bytes(int32_t num_reqs, int64_t num_tokens, int
  * out is rounded to nearest-even.
  *
  * Supported: head_dim in {8, 16, 32, 48, 64, 96, 128, 256}; block_size >= 1 (the bf16
- * matrix-core paths need block_size 16, and head_dim 64 or 128 for decode-like tiles, 128
- * for prefill chunks; other shapes use the vector path); num_heads % num_kv_heads == 0; q,
+ * matrix-core paths need block_size 16, and head_dim 48, 64 or 128 for decode-like tiles
+ * (64 or 128 on fp8 pools), 128 for prefill chunks; other shapes use the vector path, and a
+ * prefill chunk at another head_dim runs as groups of decode-like tiles); num_heads %
+ * num_kv_heads == 0; q,
  * out, caches and workspace 16-byte aligned.  workspace must hold
  * paged_attention_workspace_bytes().
  *

@@ -129,7 +129,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
                     ? pa::prefill_tile_tokens(p.g) : 0;
   p.f8 = fp8 ? 1 : 0;
   p.v16 = p.pf_tokens > 0 ? 1 : 0;
-  p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs)) ? 1 : 0;
+  p.decode_kind = (dtype == PA_DTYPE_BF16 && auto_path && pa::small_mfma_supported(D, bs, fp8)) ? 1 : 0;
   if (fp8 && p.decode_kind != 1)
     return fail(PA_ERR_DTYPE, "fp8 pools need dtype bf16, block_size 16, head_dim 64 or 128 and the automatic path");
 

@@ -45,12 +45,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBlk = 16;                      // keys per block (block_size)
 
+// head_dim 48 runs padded to 64: its rows take 128 bytes in LDS (the two padding chunks of a
+// row hold copies of real chunks and are never used), the QK^T contraction runs over 64 dims
+// with Q and K zero in dims 48..63 (set in registers), and the PV product takes 3 d tiles.
 template <int D>
 struct DecodeCfg {
-  static constexpr int KC = D / 32;           // k-chunks of the QK^T product
+  static constexpr int DP = D == 48 ? 64 : D; // contraction width and LDS row length
+  static constexpr int KC = DP / 32;          // k-chunks of the QK^T product
   static constexpr int DT = D / 16;           // 16-wide d tiles of the PV product
-  static constexpr int ROW = D * 2;           // bytes of one key row in LDS
-  static constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per row
+  static constexpr int ROW = DP * 2;          // bytes of one key row in LDS
+  static constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per LDS row
+  static constexpr int GCHUNKS = D / 8;       // 16-byte chunks per row in the pool
   static constexpr int RPI = 1024 / ROW;      // rows one direct-load instruction fills
   static constexpr int VLOADS = kBlk / RPI;   // direct-load instructions per wave per block
   static constexpr int VBUF = kBlk * ROW;     // bytes of one wave's V buffer
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
     const __bf16* qrow = q + ((int64_t)(b + tok0[u] + ni) * a.H + hkv * a.g + h0[u] + nj) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KC; ++kk) {
-      u32x4 v = col_ok[u] ? *(const u32x4*)(qrow + kdim(kk, G)) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = col_ok[u] && kdim(kk, G) < D ? *(const u32x4*)(qrow + kdim(kk, G)) : u32x4{0u, 0u, 0u, 0u};
       v ^= qsign;
       qf[u][kk] = __builtin_bit_cast(bf16x8, v);
     }
@@ -371,8 +376,15 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
       for (int u = 0; u < C::VLOADS; ++u) {
         const int r = C::RPI * u + lane / C::CHUNKS;
         const int64_t src = slot(tb, lb, r) * row_elems;
-        load_lds16(kc + src + 8 * ((lane % C::CHUNKS) ^ kswz<D>(r)), kbufw + u * 1024);
-        load_lds16(vc + src + 8 * ((lane % C::CHUNKS) ^ vswz<D>(r)), vbuf0 + u * 1024);
+        // the chunk each lane's LDS slot holds; a padding slot (head_dim 48) gets a real chunk
+        // of the same row, so every read stays inside the row
+        int ck = (lane % C::CHUNKS) ^ kswz<D>(r), cv = (lane % C::CHUNKS) ^ vswz<D>(r);
+        if constexpr (C::GCHUNKS < C::CHUNKS) {
+          ck = ck < C::GCHUNKS ? ck : ck - (C::CHUNKS - C::GCHUNKS);
+          cv = cv < C::GCHUNKS ? cv : cv - (C::CHUNKS - C::GCHUNKS);
+        }
+        load_lds16(kc + src + 8 * ck, kbufw + u * 1024);
+        load_lds16(vc + src + 8 * cv, vbuf0 + u * 1024);
       }
     };
     const float ones[4] = {1.f, 1.f, 1.f, 1.f};
@@ -382,8 +394,10 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
       bf16x8 kr[C::KC];
       bf16x4 vt[C::DT];
 #pragma unroll
-      for (int kk = 0; kk < C::KC; ++kk)
+      for (int kk = 0; kk < C::KC; ++kk) {
         kr[kk] = *(const bf16x8*)(kbufw + n * C::ROW + 16 * ((4 * kk + G) ^ kswz<D>(n)));
+        if (4 * kk + G >= C::GCHUNKS) kr[kk] = bf16x8{};             // head_dim 48: padding dims
+      }
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) vt[dt] = vt_read(vbuf0, dt);
       // the reads are done before the buffers are reloaded
@@ -467,13 +481,17 @@ hipError_t launch_small_nc(const Plan& p, const AttnArgs& a, const SmallItem* it
   const dim3 grid((unsigned)n_items, (unsigned)p.Hkv);
   if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
   else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
-  else return hipErrorInvalidValue;
+  else if (p.D != 48) return hipErrorInvalidValue;
+  else if constexpr (F8) return hipErrorInvalidValue;     // fp8 codes: head_dim 64 or 128 only
+  else hipLaunchKernelGGL((small_tile_mfma<48, false, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool small_mfma_supported(int32_t D, int32_t bs) { return bs == kBlk && (D == 64 || D == 128); }
+bool small_mfma_supported(int32_t D, int32_t bs, bool fp8) {
+  return bs == kBlk && (D == 64 || D == 128 || (D == 48 && !fp8));
+}
 
 hipError_t launch_small_mfma(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s) {
   if (p.n_small == 0) return hipSuccess;

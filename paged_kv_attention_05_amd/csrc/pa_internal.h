@@ -254,7 +254,7 @@ hipError_t launch_stage_fp8(const Plan& p, const AttnArgs& a, float scale_abs_lo
 // bf16 pools: copy the prefill requests' V blocks to fp16 (flagging, for the bf16 prefill
 // kernel, the items whose V leaves fp16's range)
 hipError_t launch_stage_v16(const Plan& p, const AttnArgs& a, void* ws, hipStream_t s);
-bool small_mfma_supported(int32_t D, int32_t bs);
+bool small_mfma_supported(int32_t D, int32_t bs, bool fp8);
 bool prefill_mfma_supported(int32_t D, int32_t bs, int32_t g);
 int32_t prefill_tile_tokens(int32_t g);
 

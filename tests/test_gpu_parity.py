@@ -142,6 +142,11 @@ EDGE = [
     # g = 4: 17 rows (68 columns) is the shortest chunk on the prefill tiles, 16 rows (64) the
     # longest on the small tiles
     ("prefill_threshold", [(100, 17), (5, 16), (0, 17), (3000, 16)], 32, 8, 128, 16, "bf16"),
+    # head_dim 48 on the matrix-core small tiles (padded to 64): decodes, grouped tiles of a
+    # chunk, a request with no context, speculative rows, key splits merged, g = 8 and g = 1
+    ("head_dim_48_mfma", [(1000, 1), (17, 1), (40, 30), (0, 64), (300, 5), (15, 1)], 8, 4, 48, 16, "bf16"),
+    ("head_dim_48_splits_g8", [(5000, 1), (9000, 1), (33, 3), (0, 1)], 32, 4, 48, 16, "bf16"),
+    ("head_dim_48_g1", [(70, 1), (5, 40), (2100, 2)], 4, 4, 48, 16, "bf16"),
 ]
 
 
@@ -530,6 +535,7 @@ WINDOW = [
     ("spec_rows_bf16", [(100, 2), (57, 3), (300, 4), (16, 5)], 8, 2, 128, 16, "bf16", (2, 7)),
     ("vector_f32", [(60, 10), (1, 1), (0, 23), (3000, 1)], 8, 2, 48, 4, "f32", (1, 5, 64, 1000)),
     ("decodes_d64_long", [(20000, 1), (9000, 1)], 8, 1, 64, 16, "bf16", (300, 5000)),
+    ("mixed_d48_bf16", [(1000, 1), (300, 3), (0, 20), (60, 40)], 8, 4, 48, 16, "bf16", (1, 100)),
 ]
 
 
@@ -680,7 +686,8 @@ def _gpu_out(batch, path=0):
     return out.float().numpy()
 
 
-@pytest.mark.parametrize("dtype,d,L", [("bf16", 128, 300), ("bf16", 128, 5000), ("f32", 48, 300), ("f32", 48, 5000)])
+@pytest.mark.parametrize("dtype,d,L", [("bf16", 128, 300), ("bf16", 128, 5000), ("bf16", 48, 300), ("f32", 48, 300),
+                                       ("f32", 48, 5000)])
 def test_gpu_chunking_invariance(dtype, d, L):
     """A prompt prefilled in one piece or in chunks of 8, 33, 64 or 4096 tokens (each step
     writes its chunk, then attends) matches the oracle's one-shot output within the bound,
