@@ -273,7 +273,11 @@ const char* paged_attn_last_error(void);
 
 /*
  * Selects the attention kernels (for tests and measurement): 0 = automatic (default),
- * 1 = vector-ALU tile kernel for every request.  Applies to later calls on this thread.
+ * 1 = vector-ALU tile kernel for every request, 2 = automatic, but with the work planner
+ * launched for every batch (by default a batch of at most 64 requests that all run on the
+ * matrix-core small tiles gets no planner launch: each workgroup of the small-tile kernel
+ * and of the split merge derives its own work item from query_start_loc and seq_lens).
+ * Applies to later calls on this thread.
  */
 void paged_attn_set_path(int32_t path);
 

@@ -124,7 +124,7 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
         return fail(PA_ERR_SHAPE, "graph_max_seq_len: request " + std::to_string(r) +
                                       " has more than 64 query columns (rows x group heads)");
   pa::set_tile_shape(p);
-  const bool auto_path = g_path == 0;
+  const bool auto_path = g_path == 0 || g_path == 2;
   p.pf_tokens = (dtype == PA_DTYPE_BF16 && auto_path && pa::prefill_mfma_supported(D, bs, p.g))
                     ? pa::prefill_tile_tokens(p.g) : 0;
   p.f8 = fp8 ? 1 : 0;
@@ -216,6 +216,9 @@ int make_plan(int32_t R, int64_t N, int32_t H, int32_t Hkv, int32_t D, int32_t b
   if (p.f8 && ng * 2 * Hkv * 16 * 4 > (int64_t)INT32_MAX) return fail(PA_ERR_SHAPE, "fp8 prefill: too many staged blocks");
   p.n_small = ns; p.n_merge = nm; p.n_pf = np; p.n_stage = ng;
   p.n_g1 = n1; p.n_g3 = n3;
+  // a small batch of decode-like requests needs no planner launch: the small kernels and the
+  // merge find their own items (one request per lane of a wave)
+  p.inline_items = (p.decode_kind == 1 && R <= pa::kInlineMaxReqs && np == 0 && g_path != 2) ? 1 : 0;
 
   size_t off = 0;
   p.off_req = off;   off = align_up(off + sizeof(pa::ReqOffsets) * (size_t)(R + 1), 256);
@@ -337,7 +340,9 @@ int attention_impl(const void* q, const void* k_cache, const void* v_cache, cons
   a.v_scale = opt.fp8 ? opt.v_scale : nullptr;
   a.scale_log2e = scale * 1.4426950408889634f;
 
-  hipError_t e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
+  hipError_t e = hipSuccess;
+  if (!p.inline_items)
+    e = timed(PA_KIND_PLAN, stream, [&] { return pa::launch_plan(p, query_start_loc, seq_lens, workspace, stream); });
   if (e == hipSuccess && p.n_pf > 0)
     e = timed(PA_KIND_PREFILL, stream, [&] {
       return p.f8 ? pa::launch_stage_fp8(p, a, std::max(std::fabs(a.scale_log2e), 1e-30f), workspace, stream)

@@ -112,7 +112,8 @@ __device__ __forceinline__ void quad_bcast4(float v, float* r) {
 // own Q^T, running max, sum and O^T, and the V^T transpose reads are shared.  Tiles of one
 // item share the split's key range, which holds without a sliding window.
 template <int D, bool F8, int NC>
-__global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs a, const SmallItem* __restrict__ items,
+__global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs a, Plan pl,
+                                                                       const SmallItem* __restrict__ items,
                                                                        int32_t total_idx, Partials part) {
   using C = DecodeCfg<D>;
   // per wave two block buffers (bf16: V and K; fp8: two V); after the key loop the same
@@ -124,8 +125,23 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
 
   const int32_t item = blockIdx.x;
   const int hkv = blockIdx.y;
-  if (item >= __builtin_amdgcn_readfirstlane(a.totals[total_idx])) return;
-  SmallItem it = items[item];
+  SmallItem it;
+  int32_t b, t, L;             // the request's first row, rows and seq_len
+  if (pl.inline_items) {       // no planner launch: the item from the batch metadata itself
+    const InlineOwner o = inline_owner(pl, a.qsl, a.seq_lens, NC == 1 ? kListSingle : kListGroup, item);
+    if (__builtin_amdgcn_readfirstlane(o.r) < 0) return;
+    it = NC == 1 ? single_item(pl, o.r, o.li, o.ns, o.o_small) : group_item(pl, o.r, o.li, o.ns, o.o_small, o.t);
+    b = __builtin_amdgcn_readfirstlane(o.q0);
+    t = __builtin_amdgcn_readfirstlane(o.t);
+    L = __builtin_amdgcn_readfirstlane(o.L);
+  } else {
+    if (item >= __builtin_amdgcn_readfirstlane(a.totals[total_idx])) return;
+    it = items[item];
+    const int32_t r = __builtin_amdgcn_readfirstlane(it.r);
+    b = __builtin_amdgcn_readfirstlane(a.qsl[r]);
+    t = __builtin_amdgcn_readfirstlane(a.qsl[r + 1]) - b;
+    L = __builtin_amdgcn_readfirstlane(a.seq_lens[r]);
+  }
   // the item is the same for the whole workgroup: scalar registers, scalar loop bounds
   it.r = __builtin_amdgcn_readfirstlane(it.r);
   it.split = __builtin_amdgcn_readfirstlane(it.split);
@@ -135,9 +151,7 @@ __global__ __launch_bounds__(256, NC == 1 ? 3 : 2) void small_tile_mfma(AttnArgs
   const int32_t ntile = NC == 1 ? 1 : __builtin_amdgcn_readfirstlane(it.ntile);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave id: uniform
   const int n = lane & 15, G = lane >> 4;
-  const int32_t b = __builtin_amdgcn_readfirstlane(a.qsl[it.r]);
-  const int32_t t = __builtin_amdgcn_readfirstlane(a.qsl[it.r + 1]) - b;
-  const int32_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[it.r]), c = L - t;
+  const int32_t c = L - t;
   const __bf16* q = (const __bf16*)a.q;
   __bf16* out = (__bf16*)a.out;
   // tile u of the item: its first token, head subset, token and head counts
@@ -479,11 +493,11 @@ hipError_t launch_small_nc(const Plan& p, const AttnArgs& a, const SmallItem* it
                            Partials part, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid((unsigned)n_items, (unsigned)p.Hkv);
-  if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
-  else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, F8, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
+  if (p.D == 128) hipLaunchKernelGGL((small_tile_mfma<128, F8, NC>), grid, dim3(256), 0, s, a, p, items, total_idx, part);
+  else if (p.D == 64) hipLaunchKernelGGL((small_tile_mfma<64, F8, NC>), grid, dim3(256), 0, s, a, p, items, total_idx, part);
   else if (p.D != 48) return hipErrorInvalidValue;
   else if constexpr (F8) return hipErrorInvalidValue;     // fp8 codes: head_dim 64 or 128 only
-  else hipLaunchKernelGGL((small_tile_mfma<48, false, NC>), grid, dim3(256), 0, s, a, items, total_idx, part);
+  else hipLaunchKernelGGL((small_tile_mfma<48, false, NC>), grid, dim3(256), 0, s, a, p, items, total_idx, part);
   return hipGetLastError();
 }
 

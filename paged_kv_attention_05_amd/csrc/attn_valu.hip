@@ -213,18 +213,32 @@ __global__ __launch_bounds__(256) void small_tile_valu(AttnArgs a, const SmallIt
 // rescaled when it grows).  A small batch's tiles have at most 8 splits: one round trip.
 constexpr int kMergeBatch = 8;
 template <typename T>
-__global__ __launch_bounds__(256) void merge_splits(AttnArgs a, const MergeItem* __restrict__ items,
+__global__ __launch_bounds__(256) void merge_splits(AttnArgs a, Plan pl, const MergeItem* __restrict__ items,
                                                     Partials part) {
   const int D = a.D;
   const int cols_per_wg = 256 / D;
   const int32_t idx = blockIdx.x / a.Hkv;
-  // the item is read together with the count: a workgroup past the count (a graph replayed
-  // with fewer items than its grid) reads a stale item inside the list and exits unused
-  const int32_t total = __builtin_amdgcn_readfirstlane(a.totals[1]);
-  const MergeItem it = items[idx];
-  asm volatile("" ::"s"(total), "s"(it.row0), "s"(it.ntok), "s"(it.hsub), "s"(it.first), "s"(it.nsplit),
-               "s"(a.g), "s"(a.tile_heads), "s"(a.H), "s"(part.m), "s"(part.l), "s"(part.acc), "s"(a.out));
-  if (idx >= total) return;
+  MergeItem it;
+  if (pl.inline_items) {       // no planner launch: the item from the batch metadata itself
+    const InlineOwner o = inline_owner(pl, a.qsl, a.seq_lens, kListMerge, idx);
+    if (__builtin_amdgcn_readfirstlane(o.r) < 0) return;
+    it = merge_item(pl, o.r, o.li, o.ns, o.o_small, o.t, o.q0);
+    it.row0 = __builtin_amdgcn_readfirstlane(it.row0);
+    it.ntok = __builtin_amdgcn_readfirstlane(it.ntok);
+    it.hsub = __builtin_amdgcn_readfirstlane(it.hsub);
+    it.first = __builtin_amdgcn_readfirstlane(it.first);
+    it.nsplit = __builtin_amdgcn_readfirstlane(it.nsplit);
+    asm volatile("" ::"s"(it.row0), "s"(it.ntok), "s"(it.hsub), "s"(it.first), "s"(it.nsplit), "s"(a.g),
+                 "s"(a.tile_heads), "s"(a.H), "s"(part.m), "s"(part.l), "s"(part.acc), "s"(a.out));
+  } else {
+    // the item is read together with the count: a workgroup past the count (a graph replayed
+    // with fewer items than its grid) reads a stale item inside the list and exits unused
+    const int32_t total = __builtin_amdgcn_readfirstlane(a.totals[1]);
+    it = items[idx];
+    asm volatile("" ::"s"(total), "s"(it.row0), "s"(it.ntok), "s"(it.hsub), "s"(it.first), "s"(it.nsplit),
+                 "s"(a.g), "s"(a.tile_heads), "s"(a.H), "s"(part.m), "s"(part.l), "s"(part.acc), "s"(a.out));
+    if (idx >= total) return;
+  }
   const int hkv = blockIdx.x % a.Hkv;
   const int col = blockIdx.y * cols_per_wg + threadIdx.x / D;
   const int d = threadIdx.x % D;
@@ -302,8 +316,8 @@ hipError_t launch_merge(const Plan& p, const AttnArgs& a, void* ws, int32_t dtyp
   Partials part{(float*)(w + p.off_pm), (float*)(w + p.off_pl), (float*)(w + p.off_pacc)};
   const int cols_per_wg = 256 / p.D;
   const dim3 grid((unsigned)(p.n_merge * p.Hkv), (unsigned)((kCols + cols_per_wg - 1) / cols_per_wg));
-  if (dtype == 0) hipLaunchKernelGGL(merge_splits<float>, grid, dim3(256), 0, s, a, items, part);
-  else hipLaunchKernelGGL(merge_splits<uint16_t>, grid, dim3(256), 0, s, a, items, part);
+  if (dtype == 0) hipLaunchKernelGGL(merge_splits<float>, grid, dim3(256), 0, s, a, p, items, part);
+  else hipLaunchKernelGGL(merge_splits<uint16_t>, grid, dim3(256), 0, s, a, p, items, part);
   return hipGetLastError();
 }
 

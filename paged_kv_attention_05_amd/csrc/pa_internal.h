@@ -60,6 +60,9 @@ struct Plan {
                                    //    pools: V converted; fp8 pools: the codes times their scales)
   int32_t graph_max;               // > 0: the call is sized for every seq_len = graph_max (the
                                    //      planner counts device lengths clamped to it)
+  int32_t inline_items;            // 1: no planner launch; the matrix-core small kernels and the
+                                   //    merge derive their own items (at most 64 requests, no
+                                   //    prefill-path request)
   int64_t n_small, n_merge, n_pf;  // item counts (host-computed); n_small counts tile-splits
   int64_t n_g1, n_g3;              // matrix-core small kernels: single-tile and grouped items
   int64_t n_stage;                 // staged blocks of the prefill requests
@@ -193,6 +196,115 @@ __host__ __device__ __forceinline__ void small_groups(const Plan& p, int32_t t, 
   const int32_t gt = group_tiles(p);
   if (tiles == 1 || gt == 1 || p.window > 0) *n1 = tiles * ns;
   else *n3 = ((tiles + gt - 1) / gt) * ns;
+}
+
+// The items of the small tiles' lists, from the owning request's exclusive offsets (the
+// planner's scans) and the item's index li within the request.  o_small: the request's first
+// tile-split index (its partials); ns: its key splits; t, q0: its query rows and first row.
+// single tile (a decode, or any request under a window or on fp8 pools): one item per
+// (tile, split); also the vector kernel's per-tile list
+__host__ __device__ __forceinline__ SmallItem single_item(const Plan& p, int32_t r, int32_t li, int32_t ns,
+                                                          int32_t o_small) {
+  const int32_t tile = li / ns;
+  SmallItem it;
+  it.r = r;
+  it.tok0 = (tile / p.hsubs) * p.tile_tokens;
+  it.hsub = tile % p.hsubs;
+  it.split = li - tile * ns;
+  it.nsplit = ns;
+  it.first = o_small + tile * ns;
+  it.tile0 = tile;
+  it.ntile = 1;
+  return it;
+}
+// group of up to group_tiles(p) consecutive tiles: one item per (group, split)
+__host__ __device__ __forceinline__ SmallItem group_item(const Plan& p, int32_t r, int32_t li, int32_t ns,
+                                                         int32_t o_small, int32_t t) {
+  const int32_t tiles = ((t + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
+  const int32_t grp = li / ns;
+  const int32_t tile0 = grp * group_tiles(p);
+  SmallItem it;
+  it.r = r;
+  it.tok0 = (tile0 / p.hsubs) * p.tile_tokens;
+  it.hsub = tile0 % p.hsubs;
+  it.split = li - grp * ns;
+  it.nsplit = ns;
+  it.first = o_small + tile0 * ns;
+  it.tile0 = tile0;
+  it.ntile = min(group_tiles(p), tiles - tile0);
+  return it;
+}
+// the merge of tile `tile` of a request with more than one split
+__host__ __device__ __forceinline__ MergeItem merge_item(const Plan& p, int32_t r, int32_t tile, int32_t ns,
+                                                         int32_t o_small, int32_t t, int32_t q0) {
+  MergeItem it;
+  it.r = r;
+  it.tok0 = (tile / p.hsubs) * p.tile_tokens;
+  it.hsub = tile % p.hsubs;
+  it.first = o_small + tile * ns;
+  it.nsplit = ns;
+  it.row0 = q0 + it.tok0;
+  it.ntok = min(p.tile_tokens, t - it.tok0);
+  it.pad0 = 0;
+  return it;
+}
+
+// Without a planner launch (Plan::inline_items: at most 64 requests, all on the small tiles)
+// every workgroup of the small kernels and of the merge finds its own item: lane r of each
+// wave counts request r with the planner's formulas, a wave prefix sum gives the offsets the
+// planner's scan would, and the lane whose range holds the item's index owns it.
+constexpr int kInlineMaxReqs = 64;
+enum InlineList { kListSingle = 0, kListGroup = 1, kListMerge = 2 };
+struct InlineOwner {
+  int32_t r;                 // -1: the index is past the list's end (the workgroup exits)
+  int32_t li;                // the item's index within its request's items
+  int32_t o_small, ns, t, q0;
+  int32_t L;                 // the request's seq_len as given (not clamped)
+};
+// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8 within each row
+// of 16 lanes (a lane with no source lane adds 0), then the last lane of row 0 added to row 1
+// and of row 2 to row 3 (row_bcast:15), then the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ InlineOwner inline_owner(const Plan& p, const int32_t* qsl, const int32_t* seq_lens,
+                                                    int list, int32_t idx) {
+  const int lane = threadIdx.x & 63;
+  int32_t t = 0, q0 = 0, n_small = 0, n_list = 0, ns = 1, Lr = 0;
+  if (lane < p.R) {
+    q0 = qsl[lane];
+    t = qsl[lane + 1] - q0;
+    Lr = seq_lens[lane];
+    // (as the planner: a call sized for a capacity counts lengths clamped to it)
+    const int32_t L = p.graph_max > 0 ? min(Lr, p.graph_max) : Lr;
+    int32_t nm, np, n1, n3;
+    request_counts(p, t, L, &n_small, &nm, &np, &ns);
+    small_groups(p, t, L, &n1, &n3);
+    n_list = list == kListSingle ? n1 : list == kListGroup ? n3 : nm;
+  }
+  const int32_t end_list = wave_inclusive_sum(n_list), end_small = wave_inclusive_sum(n_small);
+  const unsigned long long own = __ballot(idx >= end_list - n_list && idx < end_list);
+  InlineOwner o;
+  if (own == 0) {
+    o.r = -1;
+    return o;
+  }
+  const int w = __builtin_ctzll(own);                           // uniform: read the owner lane
+  o.r = w;
+  o.li = idx - __builtin_amdgcn_readlane(end_list - n_list, w);
+  o.o_small = __builtin_amdgcn_readlane(end_small - n_small, w);
+  o.ns = __builtin_amdgcn_readlane(ns, w);
+  o.t = __builtin_amdgcn_readlane(t, w);
+  o.q0 = __builtin_amdgcn_readlane(q0, w);
+  o.L = __builtin_amdgcn_readlane(Lr, w);
+  return o;
 }
 
 // Arguments common to the attention kernels.

@@ -125,69 +125,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Plan p, const int32_
     // kernel reads the two lists below)
     for (int32_t idx = cs + tid; p.decode_kind != 1 && idx < cs + tot_s; idx += kPlanThreads) {
       const int i = find_owner(o_small, n, idx);
-      const int32_t li = idx - o_small[i];
-      const int32_t ns = c_ns[i];
-      const int32_t tile = li / ns;
-      SmallItem it;
-      it.r = base + i;
-      it.tok0 = (tile / p.hsubs) * p.tile_tokens;
-      it.hsub = tile % p.hsubs;
-      it.split = li - tile * ns;
-      it.nsplit = ns;
-      it.first = o_small[i] + tile * ns;
-      it.tile0 = tile;
-      it.ntile = 1;
-      small[idx] = it;
+      small[idx] = single_item(p, base + i, idx - o_small[i], c_ns[i], o_small[i]);
     }
     // matrix-core lists: single tiles (one item per tile and split) ...
     for (int32_t idx = c1 + tid; p.decode_kind == 1 && idx < c1 + tot_1; idx += kPlanThreads) {
       const int i = find_owner(o_g1, n, idx);
-      const int32_t li = idx - o_g1[i];
-      const int32_t ns = c_ns[i];
-      const int32_t tile = li / ns;
-      SmallItem it;
-      it.r = base + i;
-      it.tok0 = (tile / p.hsubs) * p.tile_tokens;
-      it.hsub = tile % p.hsubs;
-      it.split = li - tile * ns;
-      it.nsplit = ns;
-      it.first = o_small[i] + tile * ns;
-      it.tile0 = tile;
-      it.ntile = 1;
-      g1[idx] = it;
+      g1[idx] = single_item(p, base + i, idx - o_g1[i], c_ns[i], o_small[i]);
     }
     // ... and groups of up to kGroupTiles consecutive tiles (one item per group and split)
     for (int32_t idx = c3 + tid; p.decode_kind == 1 && idx < c3 + tot_3; idx += kPlanThreads) {
       const int i = find_owner(o_g3, n, idx);
-      const int32_t li = idx - o_g3[i];
-      const int32_t ns = c_ns[i];
-      const int32_t tiles = ((c_t[i] + p.tile_tokens - 1) / p.tile_tokens) * p.hsubs;
-      const int32_t grp = li / ns;
-      const int32_t tile0 = grp * group_tiles(p);
-      SmallItem it;
-      it.r = base + i;
-      it.tok0 = (tile0 / p.hsubs) * p.tile_tokens;
-      it.hsub = tile0 % p.hsubs;
-      it.split = li - grp * ns;
-      it.nsplit = ns;
-      it.first = o_small[i] + tile0 * ns;
-      it.tile0 = tile0;
-      it.ntile = min(group_tiles(p), tiles - tile0);
-      g3[idx] = it;
+      g3[idx] = group_item(p, base + i, idx - o_g3[i], c_ns[i], o_small[i], c_t[i]);
     }
     for (int32_t idx = cm + tid; idx < cm + tot_m; idx += kPlanThreads) {
       const int i = find_owner(o_merge, n, idx);
-      const int32_t tile = idx - o_merge[i];
-      MergeItem it;
-      it.r = base + i;
-      it.tok0 = (tile / p.hsubs) * p.tile_tokens;
-      it.hsub = tile % p.hsubs;
-      it.first = o_small[i] + tile * c_ns[i];
-      it.nsplit = c_ns[i];
-      it.row0 = c_q0[i] + it.tok0;
-      it.ntok = min(p.tile_tokens, c_t[i] - it.tok0);
-      it.pad0 = 0;
-      merge[idx] = it;
+      merge[idx] = merge_item(p, base + i, idx - o_merge[i], c_ns[i], o_small[i], c_t[i], c_q0[i]);
     }
     for (int32_t idx = cp + tid; idx < cp + tot_p; idx += kPlanThreads) {
       const int i = find_owner(o_pf, n, idx);

@@ -158,6 +158,44 @@ def test_edge_case(name, specs, h, hkv, d, bs, dtype):
     H.check_batch(b, label=name)
 
 
+# ------------------------------------------------------------------- items without a planner
+INLINE = [
+    # (name, specs (computed, new), H, Hkv, D, window, pad_to)
+    ("decodes_splits", [(1000, 1), (15, 1), (300, 1), (5000, 1), (0, 1), (2100, 1)], 32, 8, 128, 0, None),
+    ("spec_rows_groups", [(100, 2), (57, 3), (300, 4), (16, 5), (2049, 9), (5000, 9)], 16, 4, 128, 0, None),
+    ("d64_window", [(20000, 1), (9000, 1), (70, 3)], 8, 1, 64, 300, None),
+    ("sixty_four_requests_d48", [(17 + (31 * i) % 900, 1 + i % 3) for i in range(64)], 8, 4, 48, 0, None),
+    ("padding_rows", [(700, 1), (90, 1), (2000, 1)], 32, 8, 128, 0, 8),
+]
+
+
+@pytest.mark.parametrize("name,specs,h,hkv,d,window,pad_to", INLINE, ids=[c[0] for c in INLINE])
+def test_inline_items_match_the_planner(name, specs, h, hkv, d, window, pad_to):
+    """A batch of at most 64 requests on the matrix-core small tiles runs without the planner
+    kernel: every workgroup of the small kernels and of the merge derives its own item.  The
+    outputs are bit-identical to those of the same call with the planner launched (path 2),
+    the planner really is skipped (no planner launch recorded), and both match the oracle."""
+    import paged_kv_attention_05_amd as pk
+    b = workloads.small_batch(specs, dtype="bf16", num_heads=h, num_kv_heads=hkv, head_dim=d,
+                              seed=zlib.crc32(name.encode()) % 1000, pad_to=pad_to)
+    assert b.num_reqs <= 64
+    launches = {}
+    outs = {}
+    for path in (0, 2):
+        pk.set_timing(True)
+        try:
+            outs[path], _, _ = H.gpu_step(b, path=path, window=window)
+            launches[path] = pk.timing_report()
+        finally:
+            pk.set_timing(False)
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    assert launches[0]["plan"][1] == 0 and launches[2]["plan"][1] == 1, launches
+    ref64, _, _ = H.oracle_step(b, window=window)
+    err = attention_error(outs[0].float().numpy(), ref64, "bf16")
+    H.log(f"[parity] inline items {name}: error {err:.3g} x bound")
+    assert err <= 1.0, err
+
+
 # ------------------------------------------------------------------------- fp8 pools
 def _fp8_pools(b):
     """The batch's context pool quantized slot by slot with the oracle's write: codes and scales."""
