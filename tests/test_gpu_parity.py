@@ -322,6 +322,39 @@ def test_fp8_prefill_v_beyond_fp16_range():
     assert err <= 1.0, err
 
 
+def test_fp8_prefill_k_beyond_fp16_range():
+    """fp8 pools whose dequantized K passes fp16's largest finite value (65504) in a few slots
+    of one request (context and a new token): the prefill kernels keep K as exact codes and
+    apply the float32 scales per score, so nothing overflows.  Those keys take (almost) all of
+    the weight of the rows whose scores they dominate, so the rows stay of ordinary size."""
+    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=38)
+    r0 = b.requests[0]
+    pool_k = b.k_cache.view(-1, b.num_kv_heads, b.head_dim)
+    for pos, hk, d, val in [(9, 1, 17, 1.2e5), (333, 6, 90, -8.0e4)]:
+        pool_k[workloads.slot_of(r0.blocks, pos, b.block_size), hk, d] = val
+    b.k[5, 3, 40] = 9.5e4                # new token 5 of request 0
+    got, ref64 = _fp8_step(b)
+    err = attention_error(got, ref64, "bf16")
+    H.log(f"[parity] fp8 prefill with K beyond fp16: error {err:.3g} x bound")
+    H.record({"case": "fp8_prefill_wide_k", "dtype": "bf16", "kv": "fp8_e4m3", "error_x_bound": err})
+    assert err <= 1.0, err
+
+
+def test_fp8_prefill_q_beyond_fp16_range():
+    """Finite query values past 65504 (bf16 holds them, fp16 does not) in prefill rows on fp8
+    pools: the QK^T product stays in bf16 on the exact codes, so the rows come out right."""
+    b = workloads.small_batch([(500, 200), (300, 150)], dtype="bf16", num_heads=32, num_kv_heads=8,
+                              head_dim=128, seed=39)
+    b.q[57, 9, 3] = 1.5e5                # request 0, row 57, query head 9 (KV head 2)
+    b.q[260, 30, 100] = -7.0e4           # request 1, row 60
+    got, ref64 = _fp8_step(b)
+    err = attention_error(got, ref64, "bf16")
+    H.log(f"[parity] fp8 prefill with q beyond fp16: error {err:.3g} x bound")
+    H.record({"case": "fp8_prefill_wide_q", "dtype": "bf16", "kv": "fp8_e4m3", "error_x_bound": err})
+    assert err <= 1.0, err
+
+
 @pytest.mark.parametrize("scale", [-0.11, 0.0])
 def test_negative_and_zero_scale_every_path(scale):
     """A negative softmax scale (applied as |scale| on -q) and a zero scale (uniform weights
