@@ -441,6 +441,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   for (int c = 0; c < 4; ++c) pb[c] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int c = 0; c < (F16 ? 1 : 4); ++c) pl[c] = u32x4{0u, 0u, 0u, 0u};
+  // bf16 pools' fast kernel: the first two V^T chunks of the next matrix phase, read by the
+  // vector phase before it (the fp8 kernel, with more registers live, measured 0.3% slower
+  // with it).  A matrix phase reads its operands from LDS with the other wave of its SIMD idle on
+  // LDS (it does vector work), and at one reading wave per SIMD LDS serves about 90 B/clk per
+  // CU, less than the products consume; the vector phase's reads run beside the other
+  // wave's, so the matrix phase starts with two of its eight operand groups in registers.
+  constexpr bool VPRE = F16 && !F8;
+  u32x4 vpre[2][C::DT];
   // V^T operand of one 16-key chunk for the four d tiles (eight transpose reads)
   auto read_v = [&](int b, int qc, u32x4* va) {
 #pragma unroll
@@ -455,11 +463,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       }
     }
   };
+  if constexpr (VPRE) {                                     // M(0) multiplies the zeroed slot by P = 0
+    read_v(NBUF - 1, 0, vpre[0]);
+    read_v(NBUF - 1, 1, vpre[1]);
+  }
   // The matrix phase as one stream of eight operand groups: the four V^T chunks of
   // O += V(i-1) P(i-1), then the four K groups of S(i) = QK^T (two k-chunks of both 32-key
   // halves, so consecutive products accumulate into different tiles).  Each group's LDS
   // reads are issued one group before its products, across the PV/QK boundary too, and
-  // scheduling fences keep that order: the matrix core does not wait on LDS.
+  // scheduling fences keep that order: the matrix core does not wait on LDS.  (VPRE: the
+  // first two groups come read ahead in vpre.)
   // One code path for every tile: at i = 0 the PV products run on a zeroed V slot with
   // P = 0, and at i = ntiles the scores of a stale K slot are never used.
   auto phase_m = [&](int32_t i, auto par) {
@@ -477,11 +490,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         }
       }
     };
-    rd(0, buf[0]);
+    if constexpr (VPRE) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) buf[0][dt] = vpre[0][dt];
+    } else {
+      rd(0, buf[0]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      if (q + 1 < 8) rd(q + 1, buf[(q + 1) & 1]);
+      if (VPRE && q == 0) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) buf[1][dt] = vpre[1][dt];
+      } else if (q + 1 < 8) {
+        rd(q + 1, buf[(q + 1) & 1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       u32x4* bb = buf[q & 1];
       if (q < 4) {
@@ -621,6 +644,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         }
         if constexpr (F8) __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // for M(i + 1): V tile i, chunks 0 and 1.  V tile i was published by the barrier at the
+    // end of slot 2i - 1 and is next overwritten by the V(i + 3) loads issued from slot 2i + 4
+    // on; this phase runs in slot 2i + 1 (A) or 2i + 2 (B), and its reads complete before the
+    // barrier that ends it (lgkmcnt(0)).
+    if constexpr (VPRE) {
+      read_v(P, 0, vpre[0]);
+      read_v(P, 1, vpre[1]);
     }
   };
 
