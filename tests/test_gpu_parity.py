@@ -309,6 +309,22 @@ def _fp8_step(b, window=0):
     return out.float().cpu().numpy(), ref64
 
 
+def test_fp8_inline_items_match_the_planner():
+    """fp8 pools, a batch of decodes and speculative rows with key splits: the call without a
+    planner launch gives the same bits as the one with it (path 2)."""
+    import paged_kv_attention_05_amd as pk
+    b = workloads.small_batch([(1000, 1), (15, 1), (5000, 1), (300, 3), (2100, 5), (0, 1)], dtype="bf16",
+                              num_heads=32, num_kv_heads=8, head_dim=128, seed=91)
+    outs = []
+    for path in (0, 2):
+        pk.set_path(path)
+        try:
+            outs.append(torch.from_numpy(_fp8_step(b)[0]))
+        finally:
+            pk.set_path(0)
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_fp8_prefill_v_beyond_fp16_range():
     """fp8 pools whose dequantized V passes fp16's largest finite value (65504) in a few
     slots of one request (context and new tokens): that request's prefill items are redone
