@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
 #pragma unroll
   for (int c = 0; c < (F16 ? 1 : 4); ++c) pl[c] = u32x4{0u, 0u, 0u, 0u};
   // bf16 pools' fast kernel: the first two V^T chunks of the next matrix phase, read by the
-  // vector phase before it (the fp8 kernel, with more registers live, measured 0.3% slower
+  // vector phase before it (the fp8 kernel, at 252 registers with it, measured 0.3-1% slower
   // with it).  A matrix phase reads its operands from LDS with the other wave of its SIMD idle on
   // LDS (it does vector work), and at one reading wave per SIMD LDS serves about 90 B/clk per
   // CU, less than the products consume; the vector phase's reads run beside the other
@@ -543,9 +543,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
   auto phase_x = [&](int32_t i, auto par) {
     constexpr int P = decltype(par)::value;
     if (i >= ntiles) return;
+    // F8: the base-2 exponents against the reference the row has now, s k - m0, one FMA per
+    // score with its key's K scale (score r of this lane is key 32sh + 8(r/4) + 4h + r%4 of
+    // the tile), before the mask so that a masked score is -inf whatever the scale.  The max
+    // below is then taken over these exponents, and the rare move of the reference shifts them.
+    const float m0 = m == kNegInf ? 0.f : m;
     if constexpr (F8) {
-      // scores times their keys' K scales (score r of this lane is key 32sh + 8(r/4) + 4h + r%4
-      // of the tile), before the mask so that a masked score is -inf whatever the scale
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
@@ -553,13 +556,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
           const f32x4 k4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(
               scoff + P * SC_TILE + 4 * (32 * sh + 8 * q));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[sh][4 * q + e] *= k4[e];
+          for (int e = 0; e < 4; ++e) s[sh][4 * q + e] = __builtin_fmaf(s[sh][4 * q + e], k4[e], -m0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);                   // keep the scale reads' registers short-lived
     }
-    // the factor from scores to base-2 exponents (F8: already in the K scales)
-    const float slx = F8 ? 1.f : sl;
     // causal mask on the diagonal tiles, window mask on the tiles holding some row's window
     // start; masked scores are -inf before the max.  This lane's score r is key kt + off + 4h.
     const int32_t kt = (i + t0) * kBK;
@@ -587,7 +588,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       mxb = fmaxf(fmaxf(mxb, s[1][r]), s[1][r + 1]);
     }
     float mx = max_xor32(fmaxf(mxa, mxb));
-    const float mxs = mx * slx;                             // mx is finite or -inf, slx > 0
+    // the row's max in base-2 exponent units (F8: the exponents were taken against m0)
+    const float mxs = F8 ? mx + m0 : mx * sl;               // mx is finite or -inf, sl > 0
     // move the reference only when the row max grew by more than kLazy (or it is unset)
     if (__builtin_amdgcn_ballot_w64(mxs > m + kLazy) != 0) {
       const float m_new = mxs > m + kLazy ? mxs : m;
@@ -597,6 +599,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
       lsum2 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+      if constexpr (F8) {
+        // the exponents against the new reference (-inf stays -inf; the shift is finite)
+        const float shift = m0 - (m == kNegInf ? 0.f : m);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[sh][r] += shift;
+        }
+      }
     }
     const float m_use = m == kNegInf ? 0.f : m;
 #pragma unroll
@@ -613,8 +624,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_tile_mfma(AttnA
         }
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj], slx, -m_use));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][8 * kh + jj + 1], slx, -m_use));
+          // (F8: s already holds the exponents)
+          const float p0 = __builtin_amdgcn_exp2f(F8 ? s[sh][8 * kh + jj] : __builtin_fmaf(s[sh][8 * kh + jj], sl, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(F8 ? s[sh][8 * kh + jj + 1]
+                                                     : __builtin_fmaf(s[sh][8 * kh + jj + 1], sl, -m_use));
           if constexpr (F16) {
             // rounded to nearest fp16 (p <= 2^kLazy, inside its range); l adds up the same
             // rounded values, so the output is an exact convex combination of V rows whose
