@@ -112,7 +112,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         eprint(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-               "this build has no multi-GPU path; the step shards by KV head or by request without "
+               "the library has no multi-GPU path; the step shards by KV head or by request without "
                "any exchange, so per-GPU throughput is the single-GPU figure.")
         return 2
 
